@@ -1,0 +1,92 @@
+"""ctypes binding of libevoattn.so: argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels.  There is no
+fallback: if the library is missing or the device is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libevoattn.so")
+
+EVO_F16 = 0
+EVO_BF16 = 1
+
+EXPORTED = (
+    "evo_attn_fwd",
+    "evo_attn_bwd",
+    "evo_attn_bwd_workspace_bytes",
+    "evo_attn_bwd_workspace_offsets",
+    "evo_status_string",
+)
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class EvoError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"evo_attn status {status}: {msg}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m evoformer_biased_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, S, I, Z = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_int, ctypes.c_size_t
+    lib.evo_attn_fwd.argtypes = [P, P, P, P, P, P, P, S, I, P]
+    lib.evo_attn_fwd.restype = I
+    lib.evo_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, S, I, P]
+    lib.evo_attn_bwd.restype = I
+    lib.evo_attn_bwd_workspace_bytes.argtypes = [S, I, I, I]
+    lib.evo_attn_bwd_workspace_bytes.restype = Z
+    lib.evo_attn_bwd_workspace_offsets.argtypes = [S, I, I, I, ctypes.POINTER(Z), ctypes.POINTER(Z), ctypes.POINTER(Z)]
+    lib.evo_attn_bwd_workspace_offsets.restype = I
+    lib.evo_status_string.argtypes = [I]
+    lib.evo_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def shape_arg(shape):
+    return (ctypes.c_int64 * 5)(*[int(x) for x in shape])
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise EvoError(status, load().evo_status_string(status).decode())
+
+
+def evo_attn_fwd(q, k, v, mask_bias, pair_bias, out, lse, shape, dtype, stream) -> int:
+    return load().evo_attn_fwd(q, k, v, mask_bias, pair_bias, out, lse, shape_arg(shape), dtype, stream)
+
+
+def evo_attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias,
+                 workspace, workspace_bytes, shape, dtype, stream) -> int:
+    return load().evo_attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias,
+                               dpair_bias, workspace, workspace_bytes, shape_arg(shape), dtype, stream)
+
+
+def evo_attn_bwd_workspace_bytes(shape, dtype, has_mask, has_pair) -> int:
+    return int(load().evo_attn_bwd_workspace_bytes(shape_arg(shape), dtype, int(has_mask), int(has_pair)))
+
+
+def evo_attn_bwd_workspace_offsets(shape, dtype, has_mask, has_pair):
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    check(load().evo_attn_bwd_workspace_offsets(shape_arg(shape), dtype, int(has_mask), int(has_pair),
+                                                ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    none = (1 << 64) - 1
+    conv = lambda x: None if x.value == none else int(x.value)
+    return conv(a), conv(b), conv(c)
+
+
+def evo_status_string(status: int) -> str:
+    return load().evo_status_string(status).decode()

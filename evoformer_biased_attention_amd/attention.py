@@ -1,0 +1,130 @@
+"""PyTorch-facing API: DS4Sci_EvoformerAttention-style call over the C ABI.
+
+torch provides device memory and the current stream; every operation runs in
+the library's HIP kernels (see _lib.py).  Interface per the DeepSpeed4Science
+guide, §3.6-§3.7: ``evoformer_attention(Q, K, V, biases)`` with ``biases`` a
+list of at most two tensors, [B,N,1,1,L] (mask) and [B,1,H,L,L] (pair); a
+missing slot is treated as absent; inputs must be fp16 or bf16 on the current
+GPU; gradients flow to Q, K, V and both biases through autograd.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float16: _lib.EVO_F16, torch.bfloat16: _lib.EVO_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check_inputs(q, k, v, mask, pair):
+    if q.dtype not in _DT:
+        raise TypeError(f"inputs must be float16 or bfloat16, got {q.dtype}")
+    for name, t in (("k", k), ("v", v), ("mask_bias", mask), ("pair_bias", pair)):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
+    if q.dim() != 5 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"Q, K, V must share one [B,N,L,H,D] shape, got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    B, N, L, H, D = q.shape
+    if mask is not None and tuple(mask.shape) != (B, N, 1, 1, L):
+        raise ValueError(f"bias 1 must be [B,N,1,1,L] = {(B, N, 1, 1, L)}, got {tuple(mask.shape)}")
+    if pair is not None and tuple(pair.shape) != (B, 1, H, L, L):
+        raise ValueError(f"bias 2 must be [B,1,H,L,L] = {(B, 1, H, L, L)}, got {tuple(pair.shape)}")
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_bias: Optional[torch.Tensor] = None,
+             pair_bias: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward: returns (out [B,N,L,H,D] dtype, lse [B,N,H,L] float32)."""
+    _check_inputs(q, k, v, mask_bias, pair_bias)
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    mask_bias = None if mask_bias is None else mask_bias.contiguous()
+    pair_bias = None if pair_bias is None else pair_bias.contiguous()
+    B, N, L, H, D = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, N, H, L), dtype=torch.float32, device=q.device)
+    _lib.check(_lib.evo_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(mask_bias), _ptr(pair_bias),
+                                 out.data_ptr(), lse.data_ptr(), q.shape, _DT[q.dtype], _stream()))
+    return out, lse
+
+
+def attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask: bool = True, want_dpair: bool = True,
+             workspace: Optional[torch.Tensor] = None) -> Dict[str, Optional[torch.Tensor]]:
+    """Backward: returns dict dq, dk, dv, dmask (or None), dpair (or None), workspace."""
+    _check_inputs(q, k, v, mask_bias, pair_bias)
+    q, k, v, out, dout = (t.contiguous() for t in (q, k, v, out, dout))
+    lse = lse.contiguous()
+    mask_bias = None if mask_bias is None else mask_bias.contiguous()
+    pair_bias = None if pair_bias is None else pair_bias.contiguous()
+    B, N, L, H, D = q.shape
+    dt = _DT[q.dtype]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dmask = torch.empty_like(mask_bias) if (mask_bias is not None and want_dmask) else None
+    dpair = torch.empty_like(pair_bias) if (pair_bias is not None and want_dpair) else None
+    nbytes = _lib.evo_attn_bwd_workspace_bytes(q.shape, dt, mask_bias is not None, pair_bias is not None)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _lib.check(_lib.evo_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(mask_bias), _ptr(pair_bias),
+                                 out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                 dv.data_ptr(), _ptr(dmask), _ptr(dpair), workspace.data_ptr(), workspace.numel(),
+                                 q.shape, dt, _stream()))
+    return {"dq": dq, "dk": dk, "dv": dv, "dmask": dmask, "dpair": dpair, "workspace": workspace}
+
+
+def workspace_f32_views(workspace: torch.Tensor, shape, dtype: torch.dtype, has_mask: bool, has_pair: bool):
+    """fp32 views of delta, dmask and dpair accumulators inside a backward workspace."""
+    B, N, L, H, D = shape
+    od, om, op = _lib.evo_attn_bwd_workspace_offsets(shape, _DT[dtype], has_mask, has_pair)
+
+    def view(off, n, shp):
+        if off is None:
+            return None
+        return workspace[off:off + 4 * n].view(torch.float32).view(*shp)
+
+    return (view(od, B * N * H * L, (B, N, H, L)),
+            view(om, B * N * L, (B, N, 1, 1, L)),
+            view(op, B * H * L * L, (B, 1, H, L, L)))
+
+
+class EvoformerFusedAttention(torch.autograd.Function):
+    """Autograd wrapper: forward saves Q, K, V, biases, O and lse; backward recomputes."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, mask_bias, pair_bias):
+        out, lse = attn_fwd(q, k, v, mask_bias, pair_bias)
+        ctx.save_for_backward(q, k, v, mask_bias, pair_bias, out, lse)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, mask_bias, pair_bias, out, lse = ctx.saved_tensors
+        want_m = mask_bias is not None and ctx.needs_input_grad[3]
+        want_p = pair_bias is not None and ctx.needs_input_grad[4]
+        g = attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_m, want_p)
+        return g["dq"], g["dk"], g["dv"], g["dmask"], g["dpair"]
+
+
+def evoformer_attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                        biases: Sequence[Optional[torch.Tensor]] = ()) -> torch.Tensor:
+    """softmax(Q K^T / sqrt(D) + biases) V over [B, N, L, H, D] tensors.
+
+    ``biases`` holds at most two tensors: [B,N,1,1,L] and [B,1,H,L,L]; a
+    missing slot is treated as absent (guide §3.7).
+    """
+    bl: List[Optional[torch.Tensor]] = list(biases)
+    if len(bl) > 2:
+        raise ValueError("at most two biases: [B,N,1,1,L] and [B,1,H,L,L]")
+    while len(bl) < 2:
+        bl.append(None)
+    return EvoformerFusedAttention.apply(Q, K, V, bl[0], bl[1])
+
+
+DS4Sci_EvoformerAttention = evoformer_attention

@@ -1,0 +1,342 @@
+// C ABI of the Evoformer attention library: argument checks, launch planning,
+// workspace layout.  Declared in include/evo_attn.h.
+//
+// Interface rules follow the DeepSpeed4Science guide, §3.7: at most two
+// biases, either may be absent; the bias shapes are [B,N,1,1,L] and
+// [B,1,H,L,L]; inputs are fp16 or bf16 and must live on the current device;
+// the backward supports head dims up to 64.  Where the guide's wrapper
+// asserts, this layer returns a status code and enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/evo_attn.h"
+#include "evo_kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// -1 unknown, 0 not gfx950, 1 gfx950
+int g_dev_ok[kMaxDevices];
+std::once_flag g_dev_once[kMaxDevices];
+
+bool device_is_gfx950(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return false;
+  std::call_once(g_dev_once[dev], [dev] {
+    hipDeviceProp_t prop;
+    g_dev_ok[dev] = 0;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+      g_dev_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 0;
+    }
+  });
+  return g_dev_ok[dev] == 1;
+}
+
+struct Shape {
+  int64_t B, N, L, H, D;
+};
+
+evo_status_t parse_shape(const int64_t* shape, int dtype, Shape* s) {
+  if (shape == nullptr) return EVO_ERR_NULL_POINTER;
+  if (dtype != EVO_F16 && dtype != EVO_BF16) return EVO_ERR_BAD_DTYPE;
+  s->B = shape[0];
+  s->N = shape[1];
+  s->L = shape[2];
+  s->H = shape[3];
+  s->D = shape[4];
+  if (s->B < 1 || s->N < 1 || s->L < 1 || s->H < 1 || s->D < 1) return EVO_ERR_BAD_SHAPE;
+  if (s->D != 8 && s->D != 16 && s->D != 32 && s->D != 64) return EVO_ERR_HEAD_DIM;
+  // every launch grid and per-slice index must fit 31 bits
+  const int64_t lim = (int64_t)1 << 30;
+  if (s->B > lim || s->N > lim || s->L > lim || s->H > lim) return EVO_ERR_BAD_SHAPE;
+  if (s->L > 65536) return EVO_ERR_BAD_SHAPE;
+  const double elems = (double)s->B * s->N * s->L * s->H * s->D;
+  const double pair = (double)s->B * s->H * s->L * s->L;
+  if (elems > 1e12 || pair > 1e12) return EVO_ERR_BAD_SHAPE;
+  const double wgs = (double)s->B * s->N * s->H * ((s->L + 31) / 32);
+  if (wgs > 2.0e9) return EVO_ERR_BAD_SHAPE;
+  return EVO_OK;
+}
+
+evo_status_t check_device_ptr(const void* p, int dev) {
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return EVO_ERR_ALIGNMENT;
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // do not leave the error for the next call
+    return EVO_ERR_NOT_DEVICE_MEMORY;
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return EVO_ERR_NOT_DEVICE_MEMORY;
+  if (attr.device != dev) return EVO_ERR_NOT_DEVICE_MEMORY;
+  return EVO_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// any output overlapping any input or another output
+bool any_alias(const Range* ins, int nin, const Range* outs, int nout) {
+  for (int o = 0; o < nout; ++o) {
+    if (outs[o].lo == 0) continue;
+    for (int i = 0; i < nin; ++i)
+      if (ins[i].lo != 0 && overlaps(outs[o], ins[i])) return true;
+    for (int p = o + 1; p < nout; ++p)
+      if (outs[p].lo != 0 && overlaps(outs[o], outs[p])) return true;
+  }
+  return false;
+}
+
+Range rng(const void* p, int64_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo ? lo + (uintptr_t)bytes : 0};
+}
+
+// ---- 16-bit encodings of sqrt(D) = hi + lo with hi <= sqrt(D) and lo >= 0
+
+uint16_t f32_to_f16_bits(float x) {
+  _Float16 h = (_Float16)x;
+  uint16_t b;
+  std::memcpy(&b, &h, 2);
+  return b;
+}
+float f16_bits_to_f32(uint16_t b) {
+  _Float16 h;
+  std::memcpy(&h, &b, 2);
+  return (float)h;
+}
+uint16_t f32_to_bf16_bits(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+float bf16_bits_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+void sqrt_split(int64_t D, bool bf16, uint16_t* hi, uint16_t* lo) {
+  const double r = std::sqrt((double)D);
+  auto enc = [bf16](double x) { return bf16 ? f32_to_bf16_bits((float)x) : f32_to_f16_bits((float)x); };
+  auto dec = [bf16](uint16_t b) { return (double)(bf16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b)); };
+  uint16_t h = enc(r);
+  if (dec(h) > r) h = (uint16_t)(h - 1);  // positive values: one step down in the encoding
+  const double rem = r - dec(h);
+  uint16_t l = rem > 0 ? enc(rem) : (uint16_t)0;
+  *hi = h;
+  *lo = l;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  int v = std::atoi(s);
+  return v > 0 ? v : dflt;
+}
+
+// slices per forward workgroup: enough workgroups to fill the chip, the rest
+// goes into reuse of the pair bias across n
+int plan_fwd_group(const Shape& s) {
+  const int64_t base = s.B * s.H * ((s.L + 127) / 128);
+  int64_t g = (s.N * base) / 1024;
+  if (g < 1) g = 1;
+  if (g > s.N) g = s.N;
+  return env_int("EVOATTN_FWD_G", (int)g);
+}
+
+// slices per bwd_q workgroup (also the dpair partial count divisor)
+int plan_bwdq_group(const Shape& s) {
+  const int64_t base = s.B * s.H * ((s.L + 31) / 32);
+  int64_t g = (s.N * base) / 1024;
+  if (g < 1) g = 1;
+  if (g > s.N) g = s.N;
+  return env_int("EVOATTN_BWD_GQ", (int)g);
+}
+
+struct WsLayout {
+  size_t delta, dmask_part, dmask_f32, dpair_part, dpair_f32, total;
+  int gq, ngq;
+};
+
+WsLayout ws_layout(const Shape& s, bool has_mask, bool has_pair) {
+  WsLayout w;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t rows = (size_t)s.B * s.N * s.H * s.L * sizeof(float);
+  w.gq = plan_bwdq_group(s);
+  w.ngq = (int)((s.N + w.gq - 1) / w.gq);
+  size_t off = 0;
+  w.delta = off;
+  off += al(rows);
+  w.dmask_part = w.dmask_f32 = (size_t)-1;
+  if (has_mask) {
+    w.dmask_part = off;
+    off += al(rows);
+    w.dmask_f32 = off;
+    off += al((size_t)s.B * s.N * s.L * sizeof(float));
+  }
+  w.dpair_part = w.dpair_f32 = (size_t)-1;
+  if (has_pair) {
+    const size_t per = (size_t)s.B * s.H * s.L * s.L * sizeof(float);
+    w.dpair_part = off;
+    off += al(per * (size_t)w.ngq);
+    w.dpair_f32 = off;
+    off += al(per);
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* evo_status_string(int status) {
+  switch (status) {
+    case EVO_OK: return "ok";
+    case EVO_ERR_NULL_POINTER: return "a required pointer is NULL (or a bias gradient was requested without its bias)";
+    case EVO_ERR_BAD_SHAPE: return "bad shape: every dimension must be >= 1 and within the supported size";
+    case EVO_ERR_BAD_DTYPE: return "bad dtype: expected EVO_F16 or EVO_BF16";
+    case EVO_ERR_HEAD_DIM: return "head dim D must be 8, 16, 32 or 64";
+    case EVO_ERR_ALIGNMENT: return "a tensor pointer is not 16-byte aligned";
+    case EVO_ERR_NOT_DEVICE_MEMORY: return "a tensor pointer is not device memory of the current device";
+    case EVO_ERR_WORKSPACE: return "workspace missing or too small";
+    case EVO_ERR_DEVICE: return "the current device is not gfx950 (MI355X)";
+    case EVO_ERR_LAUNCH: return "kernel launch failed";
+    case EVO_ERR_ALIAS: return "an output overlaps an input or another output";
+  }
+  return "unknown status";
+}
+
+evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const void* mask_bias, const void* pair_bias,
+                          void* out, float* lse, const int64_t shape[5], int dtype, void* stream) {
+  Shape s;
+  evo_status_t st = parse_shape(shape, dtype, &s);
+  if (st != EVO_OK) return st;
+  if (!q || !k || !v || !out || !lse) return EVO_ERR_NULL_POINTER;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EVO_ERR_DEVICE;
+  if (!device_is_gfx950(dev)) return EVO_ERR_DEVICE;
+  const void* ptrs[] = {q, k, v, mask_bias, pair_bias, out, lse};
+  for (const void* p : ptrs)
+    if (p && (st = check_device_ptr(p, dev)) != EVO_OK) return st;
+  const int64_t tb = s.B * s.N * s.L * s.H * s.D * 2;
+  const Range ins[] = {rng(q, tb), rng(k, tb), rng(v, tb), rng(mask_bias, s.B * s.N * s.L * 2),
+                       rng(pair_bias, s.B * s.H * s.L * s.L * 2)};
+  const Range outs[] = {rng(out, tb), rng(lse, s.B * s.N * s.H * s.L * 4)};
+  if (any_alias(ins, 5, outs, 2)) return EVO_ERR_ALIAS;
+
+  evo::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.mask = static_cast<const uint16_t*>(mask_bias);
+  a.pair = static_cast<const uint16_t*>(pair_bias);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.B = (int)s.B;
+  a.N = (int)s.N;
+  a.L = (int)s.L;
+  a.H = (int)s.H;
+  a.G = plan_fwd_group(s);
+  a.scale = (float)(1.0 / std::sqrt((double)s.D));
+  sqrt_split(s.D, dtype == EVO_BF16, &a.s_hi, &a.s_lo);
+  hipError_t e = evo::launch_fwd(a, (int)s.D, dtype == EVO_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? EVO_OK : EVO_ERR_LAUNCH;
+}
+
+size_t evo_attn_bwd_workspace_bytes(const int64_t shape[5], int dtype, int has_mask, int has_pair) {
+  Shape s;
+  if (parse_shape(shape, dtype, &s) != EVO_OK) return 0;
+  return ws_layout(s, has_mask != 0, has_pair != 0).total;
+}
+
+evo_status_t evo_attn_bwd_workspace_offsets(const int64_t shape[5], int dtype, int has_mask, int has_pair,
+                                            size_t* off_delta, size_t* off_dmask_f32, size_t* off_dpair_f32) {
+  Shape s;
+  evo_status_t st = parse_shape(shape, dtype, &s);
+  if (st != EVO_OK) return st;
+  WsLayout w = ws_layout(s, has_mask != 0, has_pair != 0);
+  if (off_delta) *off_delta = w.delta;
+  if (off_dmask_f32) *off_dmask_f32 = w.dmask_f32;
+  if (off_dpair_f32) *off_dpair_f32 = w.dpair_f32;
+  return EVO_OK;
+}
+
+evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const void* mask_bias, const void* pair_bias,
+                          const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          void* dmask_bias, void* dpair_bias, void* workspace, size_t workspace_bytes,
+                          const int64_t shape[5], int dtype, void* stream) {
+  Shape s;
+  evo_status_t st = parse_shape(shape, dtype, &s);
+  if (st != EVO_OK) return st;
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return EVO_ERR_NULL_POINTER;
+  if ((dmask_bias && !mask_bias) || (dpair_bias && !pair_bias)) return EVO_ERR_NULL_POINTER;
+  const bool has_mask = mask_bias != nullptr, has_pair = pair_bias != nullptr;
+  WsLayout w = ws_layout(s, has_mask, has_pair);
+  if (!workspace || workspace_bytes < w.total) return EVO_ERR_WORKSPACE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EVO_ERR_DEVICE;
+  if (!device_is_gfx950(dev)) return EVO_ERR_DEVICE;
+  const void* ptrs[] = {q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias, workspace};
+  for (const void* p : ptrs)
+    if (p && (st = check_device_ptr(p, dev)) != EVO_OK) return st;
+  const int64_t tb = s.B * s.N * s.L * s.H * s.D * 2;
+  const Range ins[] = {rng(q, tb),
+                       rng(k, tb),
+                       rng(v, tb),
+                       rng(mask_bias, s.B * s.N * s.L * 2),
+                       rng(pair_bias, s.B * s.H * s.L * s.L * 2),
+                       rng(out, tb),
+                       rng(lse, s.B * s.N * s.H * s.L * 4),
+                       rng(dout, tb)};
+  const Range outs[] = {rng(dq, tb),
+                        rng(dk, tb),
+                        rng(dv, tb),
+                        rng(dmask_bias, s.B * s.N * s.L * 2),
+                        rng(dpair_bias, s.B * s.H * s.L * s.L * 2),
+                        rng(workspace, (int64_t)w.total)};
+  if (any_alias(ins, 8, outs, 6)) return EVO_ERR_ALIAS;
+
+  char* ws = static_cast<char*>(workspace);
+  evo::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.mask = static_cast<const uint16_t*>(mask_bias);
+  a.pair = static_cast<const uint16_t*>(pair_bias);
+  a.out = static_cast<const uint16_t*>(out);
+  a.lse = lse;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.dmask = static_cast<uint16_t*>(dmask_bias);
+  a.dpair = static_cast<uint16_t*>(dpair_bias);
+  a.delta = reinterpret_cast<float*>(ws + w.delta);
+  a.dmask_part = has_mask ? reinterpret_cast<float*>(ws + w.dmask_part) : nullptr;
+  a.dmask_f32 = has_mask ? reinterpret_cast<float*>(ws + w.dmask_f32) : nullptr;
+  a.dpair_part = has_pair ? reinterpret_cast<float*>(ws + w.dpair_part) : nullptr;
+  a.dpair_f32 = has_pair ? reinterpret_cast<float*>(ws + w.dpair_f32) : nullptr;
+  a.B = (int)s.B;
+  a.N = (int)s.N;
+  a.L = (int)s.L;
+  a.H = (int)s.H;
+  a.Gq = w.gq;
+  a.n_groups_q = w.ngq;
+  a.scale = (float)(1.0 / std::sqrt((double)s.D));
+  sqrt_split(s.D, dtype == EVO_BF16, &a.s_hi, &a.s_lo);
+  hipError_t e = evo::launch_bwd(a, (int)s.D, dtype == EVO_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? EVO_OK : EVO_ERR_LAUNCH;
+}
+
+}  // extern "C"

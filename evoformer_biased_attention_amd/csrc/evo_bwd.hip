@@ -1,0 +1,600 @@
+// Recompute-based backward of Evoformer biased attention on gfx950.
+//
+// DeepSpeed4Science guide §3.7: the backward starts from the saved O and fp32
+// lse, derives delta, then the gradients of Q, K, V and of both biases, the
+// bias gradients accumulated in fp32 and cast back to the input dtype.
+//
+//   P   = exp(S - lse)               (S recomputed, never stored)
+//   dP  = dO V^T,  delta = rowsum(dO * O)
+//   dS  = P * (dP - delta)
+//   dV  = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K
+//   dmask[b,n,j] = sum_h sum_i dS,  dpair[b,h,i,j] = sum_n dS
+//
+// The reductions pull in different directions (dK, dV over queries; dQ over
+// keys; dpair over n; dmask over heads and queries), so the work is split:
+//   bwd_pre  delta = rowsum(dO * O), one thread per row.
+//   bwd_kv   a workgroup owns 128 keys of one (b, n, h) (32 per wave) and
+//            walks all queries: dK, dV and per-head dmask partials stay in
+//            registers.  Operands: S = Q K^T with a lane per key.
+//   bwd_q    a workgroup owns 32 queries of one (b, h) and a group of n; its
+//            4 waves split the keys.  dQ is summed over the waves in LDS per
+//            n; dpair is summed over the n of the group in registers and
+//            written once per group as an fp32 partial.  Operands:
+//            S^T = K Q^T with a lane per query.
+//   bwd_fin  dmask = sum_h partials, dpair = sum_g partials, both in a fixed
+//            order (bitwise reproducible), then rounded to dtype.
+// Both bwd_kv and bwd_q recompute P from lse; that costs one extra QK^T and
+// exp per score but keeps every reduction on chip and free of atomics.
+#include "evo_common.h"
+#include "evo_kernels.h"
+
+namespace evo {
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int D, bool HAS_MASK>
+struct BwdShape {
+  static constexpr int KSTEPS_D = (D + 15) / 16;
+  static constexpr bool AUG_IN_PAD = (D % 16) != 0;
+  static constexpr int KSTEPS = KSTEPS_D + ((HAS_MASK && !AUG_IN_PAD) ? 1 : 0);
+  static constexpr int KW = KSTEPS * 16;               // Q'/K' row width incl. mask columns
+  static constexpr int KS = padded_stride_elems(KW > 32 ? KW : 32);  // row-read + tr-read tile
+  static constexpr int VW = D < 32 ? 32 : D;
+  static constexpr int DS = padded_stride_elems(VW);   // dO / V tile stride
+  static constexpr int MB = (D + 31) / 32;
+  static constexpr int RW = KSTEPS_D * 16;             // columns read row-wise (zero beyond D)
+};
+
+// 8 values of row `row` starting at column c of a [.., D] tensor, with the
+// mask-augmentation pattern beyond D: Q side {s_hi, s_lo}, K side {m, m'}.
+template <int D>
+__device__ __forceinline__ short8_t load_row8(const uint16_t* row, int c, bool valid, bool has_mask, uint16_t aug0,
+                                              uint16_t aug1) {
+  short8_t r = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (c + 8 <= D) {
+    if (valid) r = *reinterpret_cast<const short8_t*>(row + c);
+  } else if (has_mask) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int a = c + e - D;
+      r[e] = (short)(a == 0 ? aug0 : (a == 1 ? aug1 : 0));
+    }
+  }
+  return r;
+}
+
+__device__ __forceinline__ uint16_t pick16b(const u32x2 (&b)[4], int r) {
+  uint32_t w = b[r / 4][(r % 4) / 2];
+  return (r & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
+}
+
+// ---------------------------------------------------------------- bwd_pre
+
+template <class T, int D>
+__global__ __launch_bounds__(256) void evo_bwd_pre_kernel(BwdArgs a) {
+  const int64_t rows = (int64_t)a.B * a.N * a.L * a.H;
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const int h = (int)(r % a.H);
+  const int64_t t = r / a.H;
+  const int i = (int)(t % a.L);
+  const int64_t bn = t / a.L;
+  const uint16_t* o = a.out + r * D;
+  const uint16_t* g = a.dout + r * D;
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < D; c += 8) {
+    short8_t ov = *reinterpret_cast<const short8_t*>(o + c);
+    short8_t gv = *reinterpret_cast<const short8_t*>(g + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = __builtin_fmaf(T::to_f32((uint16_t)ov[e]), T::to_f32((uint16_t)gv[e]), s);
+  }
+  a.delta[(bn * a.H + h) * a.L + i] = s;
+}
+
+// ----------------------------------------------------------------- bwd_kv
+
+constexpr int kKvWaves = 4;
+constexpr int kKvKeys = 32 * kKvWaves;
+
+template <class T, int D, bool HAS_MASK, bool HAS_PAIR, bool WANT_DMASK>
+__global__ __launch_bounds__(256, 2) void evo_bwd_kv_kernel(BwdArgs a) {
+  using S = BwdShape<D, HAS_MASK>;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[32 * S::KS];     // Q' rows of the query block (with {s_hi, s_lo})
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[32 * S::DS];    // dO rows of the query block
+  __shared__ __attribute__((aligned(16))) uint16_t sB2[HAS_PAIR ? 32 * (kKvKeys + 32) : 1];  // pair[i][j-tile]
+  __shared__ __attribute__((aligned(16))) float sNL[32];               // -lse*log2e (0 -> p = 0 rows use +inf lse)
+  __shared__ __attribute__((aligned(16))) float sDel[32];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int L = a.L, H = a.H, N = a.N;
+  const int jtiles = (L + kKvKeys - 1) / kKvKeys;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int jt = wg % jtiles;
+  int rest = wg / jtiles;
+  const int h = rest % H;
+  rest /= H;
+  const int n = rest % N;
+  const int b = rest / N;
+  const size_t slice = ((size_t)b * N + n) * L;
+  const int j = jt * kKvKeys + wave * 32 + (lane & 31);
+  const bool j_valid = j < L;
+  constexpr int B2S = kKvKeys + 32;  // 80 dwords: 4 rows hit disjoint bank octets
+
+  // ---- stationary K' and V^T operands (B of S = Q' K'^T and dP = dO V^T)
+  short8_t kop[S::KSTEPS], vop[S::KSTEPS_D];
+  {
+    const uint16_t* krow = a.k + ((slice + (j_valid ? j : 0)) * H + h) * D;
+    const uint16_t* vrow = a.v + ((slice + (j_valid ? j : 0)) * H + h) * D;
+    uint16_t m = 0;
+    if constexpr (HAS_MASK) m = j_valid ? a.mask[((size_t)b * N + n) * L + j] : (uint16_t)0;
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; ++s)
+      kop[s] = load_row8<D>(krow, 16 * s + 8 * half, j_valid, HAS_MASK, m, a.s_lo != 0 ? m : (uint16_t)0);
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS_D; ++s) vop[s] = load_row8<D>(vrow, 16 * s + 8 * half, j_valid, false, 0, 0);
+  }
+  floatx16 dk[S::MB], dv[S::MB];
+#pragma unroll
+  for (int mb = 0; mb < S::MB; ++mb) {
+    dk[mb] = floatx16{};
+    dv[mb] = floatx16{};
+  }
+  float dmask_acc = 0.f;
+
+  const int nib = (L + 31) / 32;
+  for (int ib = 0; ib < nib; ++ib) {
+    const int i0 = ib * 32;
+    __syncthreads();
+    // ---- stage the query block: Q', dO, -lse*log2e, delta, pair tile
+    for (int t = tid; t < 32 * (S::KW / 8); t += 256) {
+      int r = t / (S::KW / 8), c8 = t % (S::KW / 8);
+      int i = i0 + r;
+      const uint16_t* qrow = a.q + ((slice + (i < L ? i : 0)) * H + h) * D;
+      *reinterpret_cast<short8_t*>(&sQ[r * S::KS + c8 * 8]) =
+          load_row8<D>(qrow, c8 * 8, i < L, HAS_MASK, a.s_hi, a.s_lo);
+    }
+    for (int t = tid; t < 32 * (S::RW / 8); t += 256) {
+      int r = t / (S::RW / 8), c8 = t % (S::RW / 8);
+      int i = i0 + r;
+      short8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (i < L && c8 * 8 < D) v = *reinterpret_cast<const short8_t*>(a.dout + ((slice + i) * H + h) * D + c8 * 8);
+      *reinterpret_cast<short8_t*>(&sdO[r * S::DS + c8 * 8]) = v;
+    }
+    if (tid < 32) {
+      int i = i0 + tid;
+      float lse = (i < L) ? a.lse[(((size_t)b * N + n) * H + h) * L + i] : kNegInf;
+      // rows with lse = -inf (no finite score) get p = 0
+      sNL[tid] = (lse == kNegInf) ? kNegInf : -lse * kLog2e;
+      sDel[tid] = (i < L) ? a.delta[(((size_t)b * N + n) * H + h) * L + i] : 0.f;
+    }
+    if constexpr (HAS_PAIR) {
+      const bool vec = (L % 8) == 0;
+      for (int t = tid; t < 32 * (kKvKeys / 8); t += 256) {
+        int r = t / (kKvKeys / 8), c8 = t % (kKvKeys / 8);
+        int i = i0 + r, jj = jt * kKvKeys + c8 * 8;
+        short8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (i < L) {
+          const uint16_t* p = a.pair + (((size_t)b * H + h) * L + i) * L + jj;
+          if (vec && jj + 8 <= L) {
+            v = *reinterpret_cast<const short8_t*>(p);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (jj + e < L) ? (short)p[e] : (short)0;
+          }
+        }
+        *reinterpret_cast<short8_t*>(&sB2[r * B2S + c8 * 8]) = v;
+      }
+    }
+    __syncthreads();
+
+    // ---- S = Q' K'^T (lane = key j, rows = queries)
+    floatx16 acc = floatx16{};
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; ++s) {
+      short8_t qa = *reinterpret_cast<const short8_t*>(&sQ[(lane & 31) * S::KS + 16 * s + 8 * half]);
+      acc = T::mfma(qa, kop[s], acc);
+    }
+    floatx16 dp = floatx16{};
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS_D; ++s) {
+      short8_t oa = *reinterpret_cast<const short8_t*>(&sdO[(lane & 31) * S::DS + 16 * s + 8 * half]);
+      dp = T::mfma(oa, vop[s], dp);
+    }
+    // rows held: i = 8*(r/4) + 4*half + r%4
+    float nl[16], del[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      floatx4 x = *reinterpret_cast<const floatx4*>(&sNL[8 * q + 4 * half]);
+      floatx4 y = *reinterpret_cast<const floatx4*>(&sDel[8 * q + 4 * half]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        nl[4 * q + u] = x[u];
+        del[4 * q + u] = y[u];
+      }
+    }
+    float sv[16];
+    if constexpr (HAS_PAIR) {
+      u32x2 pb[4];
+      const int qg = lane >> 4, i16 = lane & 15;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k0 = 8 * q + 4 * half;
+        const int n0 = wave * 32 + 16 * (qg & 1);
+        short4_t v = lds_read_tr(sB2, (k0 + (i16 >> 2)) * B2S + n0 + 4 * (i16 & 3));
+        pb[q] = __builtin_bit_cast(u32x2, v);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[r] = T::fma_mix(acc[r], a.scale, pick16b(pb, r));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[r] = acc[r] * a.scale;
+    }
+    uint32_t ppk[8], dspk[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p0 = (nl[r] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], kLog2e, nl[r]));
+      float p1 = (nl[r + 1] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + 1], kLog2e, nl[r + 1]));
+      float d0 = p0 * (dp[r] - del[r]);
+      float d1 = p1 * (dp[r + 1] - del[r + 1]);
+      if constexpr (WANT_DMASK) dmask_acc += d0 + d1;
+      ppk[r / 2] = T::pack2(p0, p1);
+      dspk[r / 2] = T::pack2(d0, d1);
+    }
+    // ---- dV^T += dO^T P, dK^T += Q^T dS   (k = query, permuted as held)
+    const int qg = lane >> 4, i16 = lane & 15, g = qg >> 1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      short8_t pb = __builtin_bit_cast(short8_t, u32x4{ppk[4 * t], ppk[4 * t + 1], ppk[4 * t + 2], ppk[4 * t + 3]});
+      short8_t db = __builtin_bit_cast(short8_t, u32x4{dspk[4 * t], dspk[4 * t + 1], dspk[4 * t + 2], dspk[4 * t + 3]});
+      const int k0 = 16 * t + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < S::MB; ++mb) {
+        const int n0 = 16 * (qg & 1) + 32 * mb;
+        const int r0 = k0 + (i16 >> 2), c0 = n0 + 4 * (i16 & 3);
+        short8_t oa = cat4(lds_read_tr(sdO, r0 * S::DS + c0), lds_read_tr(sdO, (r0 + 8) * S::DS + c0));
+        dv[mb] = T::mfma(oa, pb, dv[mb]);
+        short8_t qa = cat4(lds_read_tr(sQ, r0 * S::KS + c0), lds_read_tr(sQ, (r0 + 8) * S::KS + c0));
+        dk[mb] = T::mfma(qa, db, dk[mb]);
+      }
+    }
+  }
+
+  // ---- epilogue: dK = scale * dK^T, dV; per-head dmask partial
+  if (j_valid) {
+    uint16_t* dkrow = a.dk + ((slice + j) * H + h) * D;
+    uint16_t* dvrow = a.dv + ((slice + j) * H + h) * D;
+#pragma unroll
+    for (int mb = 0; mb < S::MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = 32 * mb + 8 * q + 4 * half;
+        if (d < D) {
+          u32x2 wk, wv;
+          wk[0] = T::pack2(dk[mb][4 * q] * a.scale, dk[mb][4 * q + 1] * a.scale);
+          wk[1] = T::pack2(dk[mb][4 * q + 2] * a.scale, dk[mb][4 * q + 3] * a.scale);
+          wv[0] = T::pack2(dv[mb][4 * q], dv[mb][4 * q + 1]);
+          wv[1] = T::pack2(dv[mb][4 * q + 2], dv[mb][4 * q + 3]);
+          *reinterpret_cast<u32x2*>(dkrow + d) = wk;
+          *reinterpret_cast<u32x2*>(dvrow + d) = wv;
+        }
+      }
+  }
+  if constexpr (WANT_DMASK) {
+    const float tot = xhalf_sum(dmask_acc);
+    if (j_valid && half == 0) a.dmask_part[(((size_t)b * N + n) * H + h) * L + j] = tot;
+  }
+}
+
+// ------------------------------------------------------------------ bwd_q
+
+constexpr int kQWaves = 4;
+constexpr int kQChunk = 32 * kQWaves;  // keys staged per step; wave w takes block w
+
+template <class T, int D, bool HAS_MASK, bool HAS_PAIR, bool WANT_DPAIR, int DPC>
+__global__ __launch_bounds__(256, 2) void evo_bwd_q_kernel(BwdArgs a) {
+  using S = BwdShape<D, HAS_MASK>;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kQChunk * S::KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kQChunk * S::DS];
+  __shared__ __attribute__((aligned(16))) float sRed[kQWaves * 32 * S::MB * 32];  // dQ^T partials of the 4 waves
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int L = a.L, H = a.H, N = a.N;
+  const int iblocks = (L + 31) / 32;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int ng = wg % a.n_groups_q;
+  int rest = wg / a.n_groups_q;
+  const int ib = rest % iblocks;
+  rest /= iblocks;
+  const int h = rest % H;
+  const int b = rest / H;
+  const int i = ib * 32 + (lane & 31);
+  const bool i_valid = i < L;
+  const int n_begin = ng * a.Gq, n_end = min(N, n_begin + a.Gq);
+  const int nchunks = (L + kQChunk - 1) / kQChunk;
+
+  floatx16 dpacc[DPC > 0 ? DPC : 1];
+#pragma unroll
+  for (int c = 0; c < (DPC > 0 ? DPC : 1); ++c) dpacc[c] = floatx16{};
+
+  const uint16_t* prow = nullptr;
+  if constexpr (HAS_PAIR) prow = a.pair + (((size_t)b * H + h) * L + (i_valid ? i : 0)) * L;
+  const bool pvec = (L % 4) == 0;
+
+  for (int n = n_begin; n < n_end; ++n) {
+    const size_t slice = ((size_t)b * N + n) * L;
+    short8_t qop[S::KSTEPS], gop[S::KSTEPS_D];
+    {
+      const uint16_t* qrow = a.q + ((slice + (i_valid ? i : 0)) * H + h) * D;
+      const uint16_t* grow = a.dout + ((slice + (i_valid ? i : 0)) * H + h) * D;
+#pragma unroll
+      for (int s = 0; s < S::KSTEPS; ++s)
+        qop[s] = load_row8<D>(qrow, 16 * s + 8 * half, i_valid, HAS_MASK, a.s_hi, a.s_lo);
+#pragma unroll
+      for (int s = 0; s < S::KSTEPS_D; ++s) gop[s] = load_row8<D>(grow, 16 * s + 8 * half, i_valid, false, 0, 0);
+    }
+    float nl = kNegInf, del = 0.f;
+    if (i_valid) {
+      const size_t ri = (((size_t)b * N + n) * H + h) * L + i;
+      float lse = a.lse[ri];
+      nl = (lse == kNegInf) ? kNegInf : -lse * kLog2e;
+      del = a.delta[ri];
+    }
+    floatx16 dq[S::MB];
+#pragma unroll
+    for (int mb = 0; mb < S::MB; ++mb) dq[mb] = floatx16{};
+
+#pragma unroll
+    for (int cu = 0; cu < (DPC > 0 ? DPC : 1); ++cu) {
+      for (int c = (DPC > 0 ? cu : 0); c < (DPC > 0 ? cu + 1 : nchunks); ++c) {
+        if (c >= nchunks) break;
+        const int kc0 = c * kQChunk;
+        __syncthreads();
+        // ---- stage K' (with mask columns) and V rows of this chunk
+        for (int t = tid; t < kQChunk * (S::KW / 8); t += 256) {
+          int r = t / (S::KW / 8), c8 = t % (S::KW / 8);
+          int jj = kc0 + r;
+          const uint16_t* krow = a.k + ((slice + (jj < L ? jj : 0)) * H + h) * D;
+          uint16_t m = 0;
+          if constexpr (HAS_MASK) m = (jj < L) ? a.mask[((size_t)b * N + n) * L + jj] : (uint16_t)0;
+          *reinterpret_cast<short8_t*>(&sK[r * S::KS + c8 * 8]) =
+              load_row8<D>(krow, c8 * 8, jj < L, HAS_MASK, m, a.s_lo != 0 ? m : (uint16_t)0);
+        }
+        for (int t = tid; t < kQChunk * (S::RW / 8); t += 256) {
+          int r = t / (S::RW / 8), c8 = t % (S::RW / 8);
+          int jj = kc0 + r;
+          short8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+          if (jj < L && c8 * 8 < D) v = *reinterpret_cast<const short8_t*>(a.v + ((slice + jj) * H + h) * D + c8 * 8);
+          *reinterpret_cast<short8_t*>(&sV[r * S::DS + c8 * 8]) = v;
+        }
+        __syncthreads();
+        const int j0 = kc0 + wave * 32;
+        if (j0 < L) {
+          // ---- S^T = K' Q'^T and dP^T = V dO^T (lane = query i)
+          floatx16 acc = floatx16{}, dp = floatx16{};
+#pragma unroll
+          for (int s = 0; s < S::KSTEPS; ++s) {
+            short8_t ka = *reinterpret_cast<const short8_t*>(&sK[(wave * 32 + (lane & 31)) * S::KS + 16 * s + 8 * half]);
+            acc = T::mfma(ka, qop[s], acc);
+          }
+#pragma unroll
+          for (int s = 0; s < S::KSTEPS_D; ++s) {
+            short8_t va = *reinterpret_cast<const short8_t*>(&sV[(wave * 32 + (lane & 31)) * S::DS + 16 * s + 8 * half]);
+            dp = T::mfma(va, gop[s], dp);
+          }
+          float sv[16];
+          if constexpr (HAS_PAIR) {
+            u32x2 pb[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              int jj = j0 + 8 * q + 4 * half;
+              u32x2 v = {0u, 0u};
+              if (i_valid) {
+                if (pvec && jj + 4 <= L) {
+                  v = *reinterpret_cast<const u32x2*>(prow + jj);
+                } else {
+                  uint16_t tt[4];
+#pragma unroll
+                  for (int u = 0; u < 4; ++u) tt[u] = (jj + u < L) ? prow[jj + u] : (uint16_t)0;
+                  v[0] = (uint32_t)tt[0] | ((uint32_t)tt[1] << 16);
+                  v[1] = (uint32_t)tt[2] | ((uint32_t)tt[3] << 16);
+                }
+              }
+              pb[q] = v;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sv[r] = T::fma_mix(acc[r], a.scale, pick16b(pb, r));
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sv[r] = acc[r] * a.scale;
+          }
+          uint32_t dspk[8];
+          float ds[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int jj = j0 + 8 * (r / 4) + 4 * half + (r % 4);
+            float p = (nl == kNegInf || jj >= L) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], kLog2e, nl));
+            ds[r] = p * (dp[r] - del);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) dspk[r / 2] = T::pack2(ds[r], ds[r + 1]);
+          if constexpr (WANT_DPAIR && DPC > 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dpacc[cu][r] += ds[r];
+          } else if constexpr (WANT_DPAIR) {
+            // long rows: accumulate straight into the fp32 result (order not fixed)
+            if (i_valid) {
+              float* dst = a.dpair_f32 + (((size_t)b * H + h) * L + i) * L;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int jj = j0 + 8 * (r / 4) + 4 * half + (r % 4);
+                if (jj < L) atomicAdd(dst + jj, ds[r]);
+              }
+            }
+          }
+          // ---- dQ^T += K^T dS^T  (A = K^T by transposed reads, k = key as held)
+          const int qg = lane >> 4, i16 = lane & 15, g = qg >> 1;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            short8_t db = __builtin_bit_cast(short8_t, u32x4{dspk[4 * t], dspk[4 * t + 1], dspk[4 * t + 2], dspk[4 * t + 3]});
+            const int k0 = wave * 32 + 16 * t + 4 * g;
+#pragma unroll
+            for (int mb = 0; mb < S::MB; ++mb) {
+              const int r0 = k0 + (i16 >> 2), c0 = 16 * (qg & 1) + 32 * mb + 4 * (i16 & 3);
+              short8_t ka = cat4(lds_read_tr(sK, r0 * S::KS + c0), lds_read_tr(sK, (r0 + 8) * S::KS + c0));
+              dq[mb] = T::mfma(ka, db, dq[mb]);
+            }
+          }
+        }
+      }
+    }
+    // ---- sum the 4 waves' dQ^T partials, write dQ = scale * dQ
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < S::MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sRed[((wave * S::MB + mb) * 16 + r) * 64 + lane] = dq[mb][r];
+    __syncthreads();
+    {
+      // thread t sums element e = t (+256k) of the 16*MB*64 per-wave values
+      constexpr int E = 16 * S::MB * 64;
+      for (int e = tid; e < E; e += 256) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kQWaves; ++w) s += sRed[w * E + e];
+        const int ln = e % 64, r = (e / 64) % 16, mb = e / (64 * 16);
+        const int ii = ib * 32 + (ln & 31);
+        const int d = 32 * mb + 8 * (r / 4) + 4 * (ln >> 5) + (r % 4);
+        if (ii < L && d < D) a.dq[((slice + ii) * H + h) * D + d] = T::from_f32(s * a.scale);
+      }
+    }
+  }
+
+  if constexpr (WANT_DPAIR && DPC > 0) {
+    if (i_valid) {
+      float* dst = a.dpair_part + ((((size_t)ng * a.B + b) * H + h) * L + i) * L;
+#pragma unroll
+      for (int cu = 0; cu < DPC; ++cu) {
+        const int j0 = cu * kQChunk + wave * 32;
+        if (j0 < L) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int jj = j0 + 8 * q + 4 * half;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (jj + u < L) dst[jj + u] = dpacc[cu][4 * q + u];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bwd_fin
+
+template <class T>
+__global__ __launch_bounds__(256) void evo_bwd_fin_dmask_kernel(BwdArgs a) {
+  const int64_t total = (int64_t)a.B * a.N * a.L;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int j = (int)(e % a.L);
+  const int64_t bn = e / a.L;
+  float s = 0.f;
+  for (int h = 0; h < a.H; ++h) s += a.dmask_part[(bn * a.H + h) * a.L + j];
+  a.dmask_f32[e] = s;
+  a.dmask[e] = T::from_f32(s);
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void evo_bwd_fin_dpair_kernel(BwdArgs a, int ngroups, int from_f32) {
+  const int64_t per = (int64_t)a.B * a.H * a.L * a.L;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= per) return;
+  float s;
+  if (from_f32) {
+    s = a.dpair_f32[e];
+  } else {
+    s = 0.f;
+    for (int g = 0; g < ngroups; ++g) s += a.dpair_part[(int64_t)g * per + e];
+    a.dpair_f32[e] = s;
+  }
+  a.dpair[e] = T::from_f32(s);
+}
+
+__global__ __launch_bounds__(256) void evo_zero_f32_kernel(float* p, int64_t n) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e < n) p[e] = 0.f;
+}
+
+// ------------------------------------------------------------------ launch
+
+template <class T, int D, bool HM, bool HP>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+  const bool want_dmask = a.dmask != nullptr;
+  const bool want_dpair = a.dpair != nullptr;
+  {
+    const int64_t rows = (int64_t)a.B * a.N * a.L * a.H;
+    hipLaunchKernelGGL((evo_bwd_pre_kernel<T, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a);
+  }
+  {
+    const int grid = a.B * a.N * a.H * ((a.L + kKvKeys - 1) / kKvKeys);
+    if (want_dmask)
+      hipLaunchKernelGGL((evo_bwd_kv_kernel<T, D, HM, HP, true>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((evo_bwd_kv_kernel<T, D, HM, HP, false>), dim3(grid), dim3(256), 0, st, a);
+  }
+  {
+    const int nchunks = (a.L + kQChunk - 1) / kQChunk;
+    const int grid = a.B * a.H * ((a.L + 31) / 32) * a.n_groups_q;
+    if (!want_dpair) {
+      hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, false, 0>), dim3(grid), dim3(256), 0, st, a);
+    } else if (nchunks <= 2) {
+      hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, true, 2>), dim3(grid), dim3(256), 0, st, a);
+    } else if (nchunks <= 4) {
+      hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, true, 4>), dim3(grid), dim3(256), 0, st, a);
+    } else if (nchunks <= 6) {
+      hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, true, 6>), dim3(grid), dim3(256), 0, st, a);
+    } else {
+      const int64_t n = (int64_t)a.B * a.H * a.L * a.L;
+      hipLaunchKernelGGL(evo_zero_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dpair_f32, n);
+      hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, true, 0>), dim3(grid), dim3(256), 0, st, a);
+    }
+  }
+  if (want_dmask) {
+    const int64_t total = (int64_t)a.B * a.N * a.L;
+    hipLaunchKernelGGL(evo_bwd_fin_dmask_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
+  }
+  if (want_dpair) {
+    const int nchunks = (a.L + kQChunk - 1) / kQChunk;
+    const int64_t per = (int64_t)a.B * a.H * a.L * a.L;
+    hipLaunchKernelGGL(evo_bwd_fin_dpair_kernel<T>, dim3((unsigned)((per + 255) / 256)), dim3(256), 0, st, a,
+                       a.n_groups_q, nchunks > 6 ? 1 : 0);
+  }
+  return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
+  const bool hm = a.mask != nullptr, hp = a.pair != nullptr;
+  if (hm && hp) return launch_bwd_t<T, D, true, true>(a, s);
+  if (hm) return launch_bwd_t<T, D, true, false>(a, s);
+  if (hp) return launch_bwd_t<T, D, false, true>(a, s);
+  return launch_bwd_t<T, D, false, false>(a, s);
+}
+
+template <class T>
+static hipError_t launch_bwd_dt(const BwdArgs& a, int D, hipStream_t s) {
+  switch (D) {
+    case 8: return launch_bwd_d<T, 8>(a, s);
+    case 16: return launch_bwd_d<T, 16>(a, s);
+    case 32: return launch_bwd_d<T, 32>(a, s);
+    case 64: return launch_bwd_d<T, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(BwdArgs a, int D, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_bwd_dt<BF16>(a, D, stream) : launch_bwd_dt<F16>(a, D, stream);
+}
+
+}  // namespace evo

@@ -1,0 +1,67 @@
+// Launch interfaces between the C-ABI layer and the kernels (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace evo {
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* mask;  // [B,N,L] or null
+  const uint16_t* pair;  // [B,H,L,L] or null
+  uint16_t* out;
+  float* lse;            // [B,N,H,L]
+  int B, N, L, H;
+  int G;         // slices n per workgroup
+  int n_groups;  // ceil(N / G)
+  int i_tiles;   // query tiles per slice
+  float scale;   // 1/sqrt(D)
+  uint16_t s_hi, s_lo;  // sqrt(D) = s_hi + s_lo in the 16-bit dtype, s_lo >= 0
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* mask;
+  const uint16_t* pair;
+  const uint16_t* out;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  uint16_t* dmask;       // [B,N,L] or null
+  uint16_t* dpair;       // [B,H,L,L] or null
+  float* delta;          // [B,N,H,L]
+  float* dmask_part;     // [B,N,H,L]   (when dmask requested)
+  float* dmask_f32;      // [B,N,L]
+  float* dpair_part;     // [n_groups_q, B, H, L, L] (when dpair requested)
+  float* dpair_f32;      // [B,H,L,L]
+  int B, N, L, H;
+  int Gq;          // slices per bwd_q workgroup
+  int n_groups_q;
+  float scale;
+  uint16_t s_hi, s_lo;
+};
+
+// Map a hardware workgroup id to a logical one so that consecutive logical
+// ids run on the same XCD (the dispatcher deals ids round-robin over 8 XCDs).
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  constexpr int kXcd = 8;
+  const int per = total / kXcd;     // full rounds
+  const int tail = total - per * kXcd;
+  if (id >= per * kXcd) return id;  // ragged tail keeps its own order
+  (void)tail;
+  const int xcd = id % kXcd;
+  const int slot = id / kXcd;
+  return xcd * per + slot;
+}
+
+hipError_t launch_fwd(FwdArgs a, int D, bool bf16, hipStream_t stream);
+hipError_t launch_bwd(BwdArgs a, int D, bool bf16, hipStream_t stream);
+
+}  // namespace evo

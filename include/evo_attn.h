@@ -1,0 +1,115 @@
+/* evo_attn.h — C ABI of the MI355X (gfx950) Evoformer biased attention library.
+ *
+ * The operation is the one the DeepSpeed4Science guide describes for
+ * DS4Sci_EvoformerAttention (page "DeepSpeed4Science 技术指南"):
+ *   §3.5  reference attention: QK^T times the scale factor, plus the bias,
+ *         softmax over keys, times V;
+ *   §3.6  the tensor layouts of MSA row, MSA column and triangle attention:
+ *         Q, K, V [B, N, L, H, D]; bias 1 (a residue mask) [B, N, 1, 1, L];
+ *         bias 2 (pair bias / edges) [B, 1, H, L, L];
+ *   §3.7  at most two biases, a missing one treated as absent; the forward
+ *         keeps O and an fp32 log-sum-exp per query row; the backward derives
+ *         delta from them and returns the gradients of Q, K, V and of both
+ *         biases, the bias gradients accumulated in fp32 and cast back to the
+ *         input dtype; the backward supports head dims up to 64.
+ *
+ *   S[b,n,h,i,j] = scale * sum_d Q[b,n,i,h,d] K[b,n,j,h,d] + mask[b,n,j] + pair[b,h,i,j]
+ *   O[b,n,i,h,:] = sum_j softmax_j(S)[b,n,h,i,j] V[b,n,j,h,:]
+ *   lse[b,n,h,i] = log sum_j exp S[b,n,h,i,j]          (natural log, fp32)
+ *   scale = 1/sqrt(D).
+ *
+ * Conventions common to every entry point
+ *   - shape = {B, N, L, H, D}; B, N, L, H >= 1; D in {8, 16, 32, 64}.
+ *   - Every tensor pointer is a DEVICE pointer on the current HIP device, to
+ *     a dense row-major buffer, 16-byte aligned.  16-bit tensors hold IEEE
+ *     half (EVO_F16) or bfloat16 (EVO_BF16) values; lse is float32.
+ *   - All buffers are owned by the caller.  The library allocates no device
+ *     memory and keeps no state between calls; calls are re-entrant.
+ *   - Outputs are overwritten, never accumulated.  No output may alias an
+ *     input or another output.
+ *   - A bias pointer may be NULL: that bias is absent (treated as zero).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *     stream) and the call returns without waiting for it.
+ *   - Argument errors are detected on the host before anything is enqueued:
+ *     the call returns a non-zero status and leaves every output untouched.
+ *     A launch failure returns EVO_ERR_LAUNCH.  The library never aborts and
+ *     never prints.
+ */
+#ifndef EVO_ATTN_H
+#define EVO_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { EVO_F16 = 0, EVO_BF16 = 1 } evo_dtype_t;
+
+typedef enum {
+  EVO_OK = 0,
+  EVO_ERR_NULL_POINTER = 1,      /* a required pointer is NULL, or a bias gradient was requested without its bias */
+  EVO_ERR_BAD_SHAPE = 2,         /* a dimension < 1, or sizes that overflow 32-bit indexing */
+  EVO_ERR_BAD_DTYPE = 3,         /* dtype is neither EVO_F16 nor EVO_BF16 */
+  EVO_ERR_HEAD_DIM = 4,          /* D not in {8, 16, 32, 64} */
+  EVO_ERR_ALIGNMENT = 5,         /* a pointer is not 16-byte aligned */
+  EVO_ERR_NOT_DEVICE_MEMORY = 6, /* a pointer is not device memory of the current device */
+  EVO_ERR_WORKSPACE = 7,         /* workspace NULL or smaller than evo_attn_bwd_workspace_bytes() */
+  EVO_ERR_DEVICE = 8,            /* the current device is not gfx950 */
+  EVO_ERR_LAUNCH = 9,            /* a kernel launch failed */
+  EVO_ERR_ALIAS = 10             /* an output overlaps an input or another output */
+} evo_status_t;
+
+/* Forward (guide §3.5 and §3.7: fused attention that keeps O and the fp32 lse).
+ *   q, k, v     [B,N,L,H,D] dtype          inputs
+ *   mask_bias   [B,N,1,1,L] dtype or NULL  additive bias on keys, shared by all heads and queries
+ *   pair_bias   [B,1,H,L,L] dtype or NULL  additive bias, shared by every n
+ *   out         [B,N,L,H,D] dtype          output
+ *   lse         [B,N,H,L]   float32        natural-log log-sum-exp of each row of S
+ * A query row whose scores are all -inf gets out = 0 and lse = -inf. */
+evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const void* mask_bias,
+                          const void* pair_bias, void* out, float* lse, const int64_t shape[5],
+                          int dtype, void* stream);
+
+/* Bytes of device workspace evo_attn_bwd needs for this problem (0 on bad arguments). */
+size_t evo_attn_bwd_workspace_bytes(const int64_t shape[5], int dtype, int has_mask, int has_pair);
+
+/* Byte offsets into the workspace, valid after evo_attn_bwd returns and its
+ * work completes, of the fp32 accumulators the bias gradients are cast from:
+ *   delta      [B,N,H,L]   rowsum(dO * O)
+ *   dmask_f32  [B,N,L]     sum over h and i of dS          (only if has_mask)
+ *   dpair_f32  [B,H,L,L]   sum over n of dS                (only if has_pair)
+ * An offset is set to (size_t)-1 when that accumulator is absent.
+ * Returns EVO_OK or an argument error. */
+evo_status_t evo_attn_bwd_workspace_offsets(const int64_t shape[5], int dtype, int has_mask,
+                                            int has_pair, size_t* off_delta, size_t* off_dmask_f32,
+                                            size_t* off_dpair_f32);
+
+/* Backward (guide §3.7: recompute from lse, derive delta, then the gradients).
+ *   q, k, v, mask_bias, pair_bias  as passed to evo_attn_fwd
+ *   out, lse                       exactly as evo_attn_fwd wrote them
+ *   dout        [B,N,L,H,D] dtype  gradient of the loss w.r.t. out
+ *   dq, dk, dv  [B,N,L,H,D] dtype  outputs
+ *   dmask_bias  [B,N,1,1,L] dtype  output: sum over h and i of dS; may be NULL (not computed)
+ *   dpair_bias  [B,1,H,L,L] dtype  output: sum over n of dS;       may be NULL (not computed)
+ *   workspace, workspace_bytes     device scratch of at least evo_attn_bwd_workspace_bytes(),
+ *                                  contents undefined on entry; see evo_attn_bwd_workspace_offsets
+ * The bias gradients are accumulated in fp32 in a fixed order (the result
+ * is bitwise reproducible) and rounded to dtype to nearest even.
+ * Passing dmask_bias without mask_bias, or dpair_bias without pair_bias, is
+ * EVO_ERR_NULL_POINTER. */
+evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const void* mask_bias,
+                          const void* pair_bias, const void* out, const float* lse, const void* dout,
+                          void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias,
+                          void* workspace, size_t workspace_bytes, const int64_t shape[5], int dtype,
+                          void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* evo_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EVO_ATTN_H */

@@ -199,15 +199,14 @@ def dpair_rows(q, k, v, mask_bias, pair_bias, dout, rows: Sequence[Tuple[int, in
     scale = _scale(D)
     res = np.zeros((len(rows), L))
     for r, (b, h, i) in enumerate(rows):
-        for n in range(N):
-            s = scale * (k[b, n, :, h, :] @ q[b, n, i, h, :])  # [L]
-            if mask_bias is not None:
-                s = s + mask_bias[b, n, 0, 0, :]
-            if pair_bias is not None:
-                s = s + pair_bias[b, 0, h, i, :]
-            p, _ = _softmax_rows(s[None, :])
-            p = p[0]
-            dp = v[b, n, :, h, :] @ dout[b, n, i, h, :]
-            delta = (p * dp).sum()
-            res[r] += p * (dp - delta)
+        # all n at once: S[n, j] for the fixed query row i of head h
+        s = scale * np.einsum("njd,nd->nj", k[b, :, :, h, :], q[b, :, i, h, :])
+        if mask_bias is not None:
+            s = s + mask_bias[b, :, 0, 0, :]
+        if pair_bias is not None:
+            s = s + pair_bias[b, 0, h, i, :][None, :]
+        p, _ = _softmax_rows(s)
+        dp = np.einsum("njd,nd->nj", v[b, :, :, h, :], dout[b, :, i, h, :])
+        delta = (p * dp).sum(axis=-1, keepdims=True)
+        res[r] = (p * (dp - delta)).sum(axis=0)
     return res
