@@ -1,0 +1,262 @@
+"""Benchmark: Evoformer biased attention fwd+bwd on one MI355X.
+
+A step is one forward and one backward (all of the hot path: fused forward,
+delta, key-stationary and query-stationary backward kernels, bias-gradient
+reductions) over the MSA-row workload Q,K,V [1,256,256,4,32] fp16 with a 5%
+key mask and an N(0,1) pair bias (synthetic, seeded).  Inputs are resident in
+HBM before the timed region.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload msa_row]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+METRIC = "fwd+bwd TFLOP/s & % MFMA peak, Evoformer attn (1,256,256,4,32) fp16"
+
+# MFMA flops each kernel must do per score (D = head dim): the GEMMs it
+# performs on the score tile to produce its outputs.
+KERNEL_FLOPS_PER_SCORE = {
+    "fwd": lambda D: 4 * D,      # S = QK^T, O += PV
+    "bwd_kv": lambda D: 8 * D,   # S, dP = dO V^T, dV += P^T dO, dK += dS^T Q
+    "bwd_q": lambda D: 6 * D,    # S, dP, dQ += dS K
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="msa_row")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def kernel_sources_sha():
+    h = hashlib.sha256()
+    for f in ("evo_common.h", "evo_fwd.hip", "evo_bwd.hip", "evo_api.hip", "evo_kernels.h"):
+        with open(os.path.join(ROOT, "evoformer_biased_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def load_traffic(kernel, workload, sha):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on these sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    rec = t.get(f"{kernel}:{workload}")
+    if not rec or rec.get("sources_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, bits, seconds):
+    """The fp64 oracle, as it stands, on a bounded sample of slices of the same workload."""
+    import numpy as np
+
+    from evoformer_biased_attention_amd import inputs as I
+    from oracle import evo_oracle as O
+
+    x = I.as_float64(bits, cfg.dtype)
+    per_slice = 3.5 * 4 * cfg.H * cfg.L * cfg.L * cfg.D  # fwd + bwd flops of one (b, n) slice
+    done, t0 = 0, time.perf_counter()
+    n = 0
+    while True:
+        ns = [(n + t) % cfg.N for t in range(8)]
+        O.attention_fwd(x["q"], x["k"], x["v"], x["mask_bias"], x["pair_bias"], ns=ns)
+        O.attention_bwd(x["q"], x["k"], x["v"], x["mask_bias"], x["pair_bias"], x["dout"], ns=ns)
+        done += len(ns) * cfg.B
+        n += 8
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    return {
+        "value": per_slice * done / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} (b,n)-slice evaluations (cycling over the {cfg.B * cfg.N} slices of {cfg.name}), fwd+bwd in float64, {el:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only: the hot path has no multi-GPU part in this build "
+              f"(asked for --gpus {args.gpus}); N-sharding would split dim 1 with one dpair all-reduce.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from evoformer_biased_attention_amd import _lib
+    from evoformer_biased_attention_amd import inputs as I
+    from evoformer_biased_attention_amd.attention import attn_bwd, attn_fwd
+
+    cfg = I.CONFIGS[args.workload]
+    bits = I.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+    import numpy as np
+
+    def dev_t(b):
+        return None if b is None else torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(tdt)
+
+    q, k, v, m, p, do = (dev_t(bits[n]) for n in ("q", "k", "v", "mask_bias", "pair_bias", "dout"))
+    torch.cuda.synchronize()
+
+    ws = None
+    state = {}
+
+    def step():
+        nonlocal ws
+        out, lse = attn_fwd(q, k, v, m, p)
+        g = attn_bwd(q, k, v, m, p, out, lse, do, workspace=ws)
+        ws = g["workspace"]
+        state["out"], state["lse"] = out, lse
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K full steps, per-kernel HIP events recorded by the library on this stream
+    _lib.evo_attn_profile_read()  # drop anything recorded before
+    _lib.evo_attn_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    _lib.evo_attn_profile_enable(False)
+    ms_step = e0.elapsed_time(e1) / args.steps
+    kern = _lib.evo_attn_profile_read()
+
+    # ---- fwd-only and bwd-only loops (the pages' fwd/bwd split)
+    out, lse = state["out"], state["lse"]
+    e0.record()
+    for _ in range(args.steps):
+        attn_fwd(q, k, v, m, p)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_fwd = e0.elapsed_time(e1) / args.steps
+    e0.record()
+    for _ in range(args.steps):
+        attn_bwd(q, k, v, m, p, out, lse, do, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_bwd = e0.elapsed_time(e1) / args.steps
+
+    F = cfg.fwd_flops
+    tf_step = 3.5 * F / (ms_step * 1e-3) / 1e12
+    tf_fwd = F / (ms_fwd * 1e-3) / 1e12
+    tf_bwd = 2.5 * F / (ms_bwd * 1e-3) / 1e12
+
+    # ---- roofline of the dominant kernel
+    sha = kernel_sources_sha()
+    kernels = {name: {"avg_us": 1e3 * ms / n, "launches": n, "share": 0.0} for name, (ms, n) in kern.items() if n}
+    tot = sum(v_["avg_us"] * v_["launches"] for v_ in kernels.values()) or 1.0
+    for v_ in kernels.values():
+        v_["share"] = v_["avg_us"] * v_["launches"] / tot
+    dom = max((n for n in kernels if n in KERNEL_FLOPS_PER_SCORE), key=lambda n: kernels[n]["share"])
+    flops_launch = KERNEL_FLOPS_PER_SCORE[dom](cfg.D) * cfg.scores
+    achieved = flops_launch / (kernels[dom]["avg_us"] * 1e-6) / 1e12
+    roofline = {
+        "kernel": dom,
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_MFMA_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+        "traffic": load_traffic(dom, cfg.name, sha),
+        "flops_per_launch": flops_launch,
+        "avg_launch_us": round(kernels[dom]["avg_us"], 2),
+    }
+
+    # ---- saved activations: ours (O + lse) vs a materialised-scores path (P kept for backward)
+    B, N, L, H, D = cfg.shape
+    esz = 2
+    ours_saved = out.numel() * esz + lse.numel() * 4
+    mat_saved = B * N * H * L * L * esz
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    o2, l2 = attn_fwd(q, k, v, m, p)
+    torch.cuda.synchronize()
+    ours_peak = torch.cuda.max_memory_allocated() - base
+    del o2, l2
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    with torch.no_grad():
+        qh, kh, vh = (t.permute(0, 1, 3, 2, 4).contiguous() for t in (q, k, v))
+        s = torch.matmul(qh, kh.transpose(-1, -2).contiguous()) * (D ** -0.5)
+        if m is not None:
+            s = s + m
+        if p is not None:
+            s = s + p
+        pm = torch.softmax(s, dim=-1)
+        del s
+        om = torch.matmul(pm, vh)
+    torch.cuda.synchronize()
+    mat_peak = torch.cuda.max_memory_allocated() - base
+    del qh, kh, vh, pm, om
+
+    res = {
+        "metric": METRIC,
+        "value": round(tf_step, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: Q,K,V {list(cfg.shape)} {cfg.dtype}, mask p={cfg.mask_p}, "
+                        f"pair sigma={cfg.pair_sigma}, seed {cfg.seed}",
+            "B": B, "N": N, "L": L, "H": H, "D": D,
+        },
+        "pct_mfma_peak": round(100 * tf_step / PEAK_MFMA_TFLOPS, 2),
+        "fwd": {"ms": round(ms_fwd, 5), "tflops": round(tf_fwd, 2), "pct_peak": round(100 * tf_fwd / PEAK_MFMA_TFLOPS, 2)},
+        "bwd": {"ms": round(ms_bwd, 5), "tflops": round(tf_bwd, 2), "pct_peak": round(100 * tf_bwd / PEAK_MFMA_TFLOPS, 2)},
+        "kernels": {n: {"avg_us": round(v_["avg_us"], 2), "launches": v_["launches"], "share": round(v_["share"], 3)}
+                    for n, v_ in kernels.items()},
+        "roofline": roofline,
+        "memory": {"saved_bytes_ours": ours_saved, "saved_bytes_materialised": mat_saved,
+                   "fwd_peak_bytes_ours": int(ours_peak), "fwd_peak_bytes_materialised": int(mat_peak),
+                   "ratio_saved": round(mat_saved / ours_saved, 2)},
+        "kernel_sources_sha256": sha,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, bits, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,11 @@ EXPORTED = (
     "evo_attn_bwd_workspace_bytes",
     "evo_attn_bwd_workspace_offsets",
     "evo_status_string",
+    "evo_attn_profile_enable",
+    "evo_attn_profile_read",
+    "evo_attn_profile_kernel_name",
 )
+PROFILE_KINDS = 5
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -52,6 +56,12 @@ def load() -> ctypes.CDLL:
     lib.evo_attn_bwd_workspace_offsets.restype = I
     lib.evo_status_string.argtypes = [I]
     lib.evo_status_string.restype = ctypes.c_char_p
+    lib.evo_attn_profile_enable.argtypes = [I]
+    lib.evo_attn_profile_enable.restype = I
+    lib.evo_attn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    lib.evo_attn_profile_read.restype = I
+    lib.evo_attn_profile_kernel_name.argtypes = [I]
+    lib.evo_attn_profile_kernel_name.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -90,3 +100,15 @@ def evo_attn_bwd_workspace_offsets(shape, dtype, has_mask, has_pair):
 
 def evo_status_string(status: int) -> str:
     return load().evo_status_string(status).decode()
+
+
+def evo_attn_profile_enable(on: bool) -> bool:
+    return bool(load().evo_attn_profile_enable(int(on)))
+
+
+def evo_attn_profile_read():
+    """{kernel name: (total_ms, launches)} since the previous read."""
+    ms = (ctypes.c_double * PROFILE_KINDS)()
+    n = (ctypes.c_int64 * PROFILE_KINDS)()
+    check(load().evo_attn_profile_read(ms, n))
+    return {load().evo_attn_profile_kernel_name(k).decode(): (float(ms[k]), int(n[k])) for k in range(PROFILE_KINDS)}

@@ -15,6 +15,10 @@
 
 #include "../../include/evo_attn.h"
 #include "evo_kernels.h"
+#include "evo_prof.h"
+
+#include <atomic>
+#include <vector>
 
 namespace {
 
@@ -198,6 +202,59 @@ WsLayout ws_layout(const Shape& s, bool has_mask, bool has_pair) {
 
 }  // namespace
 
+
+// ------------------------------------------------------------ instrumentation
+
+namespace evo {
+namespace {
+std::atomic<int> g_prof_on{0};
+std::mutex g_prof_mu;
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+std::vector<hipEvent_t> g_prof_pool;  // free events
+std::vector<ProfRec> g_prof_recs;     // recorded launches not yet read
+constexpr size_t kProfMaxRecs = 1 << 16;
+int g_prof_open_kind = -1;
+hipEvent_t g_prof_open_ev = nullptr;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+void prof_begin(KernelKind k, hipStream_t s) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (g_prof_recs.size() >= kProfMaxRecs) return;
+  hipEvent_t e = prof_event();
+  if (!e) return;
+  hipEventRecord(e, s);
+  g_prof_open_kind = (int)k;
+  g_prof_open_ev = e;
+}
+
+void prof_end(KernelKind k, hipStream_t s) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (g_prof_open_kind != (int)k || !g_prof_open_ev) return;
+  hipEvent_t e = prof_event();
+  if (!e) return;
+  hipEventRecord(e, s);
+  g_prof_recs.push_back(ProfRec{(int)k, g_prof_open_ev, e});
+  g_prof_open_kind = -1;
+  g_prof_open_ev = nullptr;
+}
+}  // namespace evo
+
 extern "C" {
 
 const char* evo_status_string(int status) {
@@ -337,6 +394,46 @@ evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const voi
   sqrt_split(s.D, dtype == EVO_BF16, &a.s_hi, &a.s_lo);
   hipError_t e = evo::launch_bwd(a, (int)s.D, dtype == EVO_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? EVO_OK : EVO_ERR_LAUNCH;
+}
+
+int evo_attn_profile_enable(int on) {
+  int prev = evo::g_prof_on.exchange(on ? 1 : 0);
+  return prev;
+}
+
+evo_status_t evo_attn_profile_read(double total_ms[EVO_PROFILE_KINDS], int64_t launches[EVO_PROFILE_KINDS]) {
+  if (!total_ms || !launches) return EVO_ERR_NULL_POINTER;
+  std::lock_guard<std::mutex> lk(evo::g_prof_mu);
+  for (int k = 0; k < EVO_PROFILE_KINDS; ++k) {
+    total_ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  evo_status_t st = EVO_OK;
+  for (auto& r : evo::g_prof_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      (void)hipGetLastError();
+      st = EVO_ERR_LAUNCH;
+    } else if (r.kind >= 0 && r.kind < EVO_PROFILE_KINDS) {
+      total_ms[r.kind] += ms;
+      launches[r.kind] += 1;
+    }
+    evo::g_prof_pool.push_back(r.a);
+    evo::g_prof_pool.push_back(r.b);
+  }
+  evo::g_prof_recs.clear();
+  return st;
+}
+
+const char* evo_attn_profile_kernel_name(int kind) {
+  switch (kind) {
+    case evo::K_FWD: return "fwd";
+    case evo::K_BWD_PRE: return "bwd_pre";
+    case evo::K_BWD_KV: return "bwd_kv";
+    case evo::K_BWD_Q: return "bwd_q";
+    case evo::K_BWD_FIN: return "bwd_fin";
+  }
+  return "unknown";
 }
 
 }  // extern "C"

@@ -27,6 +27,7 @@
 // exp per score but keeps every reduction on chip and free of atomics.
 #include "evo_common.h"
 #include "evo_kernels.h"
+#include "evo_prof.h"
 
 namespace evo {
 
@@ -534,18 +535,27 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   const bool want_dpair = a.dpair != nullptr;
   {
     const int64_t rows = (int64_t)a.B * a.N * a.L * a.H;
+    prof_begin(K_BWD_PRE, st);
     hipLaunchKernelGGL((evo_bwd_pre_kernel<T, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a);
+    prof_end(K_BWD_PRE, st);
   }
   {
     const int grid = a.B * a.N * a.H * ((a.L + kKvKeys - 1) / kKvKeys);
+    prof_begin(K_BWD_KV, st);
     if (want_dmask)
       hipLaunchKernelGGL((evo_bwd_kv_kernel<T, D, HM, HP, true>), dim3(grid), dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((evo_bwd_kv_kernel<T, D, HM, HP, false>), dim3(grid), dim3(256), 0, st, a);
+    prof_end(K_BWD_KV, st);
   }
   {
     const int nchunks = (a.L + kQChunk - 1) / kQChunk;
     const int grid = a.B * a.H * ((a.L + 31) / 32) * a.n_groups_q;
+    if (want_dpair && nchunks > 6) {
+      const int64_t n = (int64_t)a.B * a.H * a.L * a.L;
+      hipLaunchKernelGGL(evo_zero_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dpair_f32, n);
+    }
+    prof_begin(K_BWD_Q, st);
     if (!want_dpair) {
       hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, false, 0>), dim3(grid), dim3(256), 0, st, a);
     } else if (nchunks <= 2) {
@@ -555,11 +565,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     } else if (nchunks <= 6) {
       hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, true, 6>), dim3(grid), dim3(256), 0, st, a);
     } else {
-      const int64_t n = (int64_t)a.B * a.H * a.L * a.L;
-      hipLaunchKernelGGL(evo_zero_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dpair_f32, n);
       hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, true, 0>), dim3(grid), dim3(256), 0, st, a);
     }
+    prof_end(K_BWD_Q, st);
   }
+  prof_begin(K_BWD_FIN, st);
   if (want_dmask) {
     const int64_t total = (int64_t)a.B * a.N * a.L;
     hipLaunchKernelGGL(evo_bwd_fin_dmask_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
@@ -570,6 +580,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(evo_bwd_fin_dpair_kernel<T>, dim3((unsigned)((per + 255) / 256)), dim3(256), 0, st, a,
                        a.n_groups_q, nchunks > 6 ? 1 : 0);
   }
+  prof_end(K_BWD_FIN, st);
   return hipGetLastError();
 }
 

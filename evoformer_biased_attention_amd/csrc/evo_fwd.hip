@@ -26,6 +26,7 @@
 //   the accumulator is rarely rescaled.
 #include "evo_common.h"
 #include "evo_kernels.h"
+#include "evo_prof.h"
 
 namespace evo {
 
@@ -306,11 +307,13 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
 template <class T, int D, bool HM, bool HP>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int grid = a.B * a.H * a.i_tiles * a.n_groups;
+  prof_begin(K_FWD, stream);
   if (HP && a.L <= 256) {
     hipLaunchKernelGGL((evo_fwd_kernel<T, D, HM, HP, 8>), dim3(grid), dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL((evo_fwd_kernel<T, D, HM, HP, 0>), dim3(grid), dim3(256), 0, stream, a);
   }
+  prof_end(K_FWD, stream);
   return hipGetLastError();
 }
 

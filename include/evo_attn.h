@@ -108,6 +108,19 @@ evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const voi
 /* Static text for a status code (never NULL). */
 const char* evo_status_string(int status);
 
+/* ---- Optional instrumentation (measurement only; does not change results).
+ * When enabled, the library records a pair of hipEvents on the caller's stream
+ * around each of its kernel launches; evo_attn_profile_read waits for the
+ * recorded launches and returns, per kernel kind, the summed elapsed time and
+ * the launch count since the previous read, then forgets them.
+ * Kinds: 0 fwd, 1 bwd_pre (delta), 2 bwd_kv (dK, dV, dmask partials),
+ *        3 bwd_q (dQ, dpair partials), 4 bwd_fin (bias-gradient reductions).
+ * At most 65536 launches are kept between reads; later ones are not recorded. */
+#define EVO_PROFILE_KINDS 5
+int evo_attn_profile_enable(int on); /* returns the previous setting */
+evo_status_t evo_attn_profile_read(double total_ms[EVO_PROFILE_KINDS], int64_t launches[EVO_PROFILE_KINDS]);
+const char* evo_attn_profile_kernel_name(int kind); /* static text, never NULL */
+
 #ifdef __cplusplus
 }
 #endif
