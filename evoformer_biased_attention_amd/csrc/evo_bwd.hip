@@ -110,11 +110,12 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_kv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
   const int L = a.L, H = a.H, N = a.N;
   const int jtiles = (L + kKvKeys - 1) / kKvKeys;
+  // h fastest, then key tile, then n: one XCD covers whole rows of a run of slices
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int jt = wg % jtiles;
-  int rest = wg / jtiles;
-  const int h = rest % H;
-  rest /= H;
+  const int h = wg % H;
+  int rest = wg / H;
+  const int jt = rest % jtiles;
+  rest /= jtiles;
   const int n = rest % N;
   const int b = rest / N;
   const size_t slice = ((size_t)b * N + n) * L;
@@ -303,12 +304,12 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_q_kernel(BwdArgs a) {
   const int L = a.L, H = a.H, N = a.N;
   const int iblocks = (L + 31) / 32;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int ng = wg % a.n_groups_q;
-  int rest = wg / a.n_groups_q;
+  const int h = wg % H;
+  int rest = wg / H;
   const int ib = rest % iblocks;
   rest /= iblocks;
-  const int h = rest % H;
-  const int b = rest / H;
+  const int ng = rest % a.n_groups_q;
+  const int b = rest / a.n_groups_q;
   const int i = ib * 32 + (lane & 31);
   const bool i_valid = i < L;
   const int n_begin = ng * a.Gq, n_end = min(N, n_begin + a.Gq);
@@ -491,6 +492,283 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_q_kernel(BwdArgs a) {
   }
 }
 
+// ----------------------------------------------------------------- bwd_q2
+//
+// Query-stationary backward for rows that fit one key tile (L <= KVTile::CH),
+// on 16x16x32 MFMA tiles so that a wave owns 16 queries:
+//   workgroup = 4 waves = 64 queries of one (b, h) and a group of n;
+//   per n, K and V of the slice arrive in LDS by asynchronous copies
+//   (double-buffered, prefetched one slice ahead), and each wave walks all
+//   keys 32 at a time:
+//     S^T = K Q^T and dP^T = V dO^T (lane = query, 4 keys per 16-key block),
+//     P = exp(S - lse), dS^T = P (dP^T - delta),
+//     dQ^T += K^T dS^T (K^T by transposed LDS reads),
+//     dpair^T += dS^T, accumulated by an MFMA against a 0/1 selection matrix
+//     so that the n-sum costs no VALU work; it stays in registers for the
+//     whole n-group and is written once as an fp32 partial.
+constexpr int kQ2Rows = 64;
+
+template <class T, int D, bool HAS_MASK, bool HAS_PAIR, bool WANT_DPAIR>
+__global__ __launch_bounds__(256, 2) void evo_bwd_q2_kernel(BwdArgs a) {
+  using TL = KVTile<D>;
+  constexpr int KS32 = (D + 31) / 32;       // 32-wide k-steps over d
+  constexpr bool AUG_PAD = (D % 32) != 0;   // D = 8, 16: mask slots follow d in the last step
+  constexpr int KSTEPS = KS32 + ((HAS_MASK && !AUG_PAD) ? 1 : 0);
+  constexpr int NB = TL::CH / 16;           // 16-key blocks per tile
+  constexpr int MB = (D + 15) / 16;         // 16-row blocks of dQ^T
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) uint16_t smask[2][TL::CH];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int L = a.L, H = a.H, N = a.N;
+  const int itiles = (L + kQ2Rows - 1) / kQ2Rows;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = wg % H;
+  int rest = wg / H;
+  const int it = rest % itiles;
+  rest /= itiles;
+  const int ng = rest % a.n_groups_q;
+  const int b = rest / a.n_groups_q;
+  const int i = it * kQ2Rows + wave * 16 + col;
+  const bool i_valid = i < L;
+  const int ic = min(i, L - 1);
+  const int n_begin = ng * a.Gq, n_end = min(N, n_begin + a.Gq);
+  const int ntiles = n_end - n_begin;
+
+  // resident pair bias: block blk, lane gets pair[ic][16 blk + 4 g + 0..3]
+  u32x2 pbias[HAS_PAIR ? NB : 1];
+  if constexpr (HAS_PAIR) {
+    const uint16_t* prow = a.pair + (((size_t)b * H + h) * L + ic) * L;
+    const bool pvec = (L % 4) == 0;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const int j = 16 * blk + 4 * g;
+      u32x2 v;
+      if (pvec) {
+        v = *reinterpret_cast<const u32x2*>(prow + min(j, L - 4));
+      } else {
+        uint32_t t4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) t4[u] = prow[min(j + u, L - 1)];
+        v[0] = t4[0] | (t4[1] << 16);
+        v[1] = t4[2] | (t4[3] << 16);
+      }
+      pbias[blk] = v;
+    }
+  }
+  // 0/1 selection operands: slot e of lane group g is key 4g + (e & 3) of block e / 4
+  short8_t sel[2];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    sel[0][e] = (e < 4 && 4 * g + e == col) ? T::one() : (short)0;
+    sel[1][e] = (e >= 4 && 4 * g + (e - 4) == col) ? T::one() : (short)0;
+  }
+  short8_t qaug = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (HAS_MASK && g == 0) {
+    qaug[0] = (short)a.s_hi;
+    qaug[1] = (short)a.s_lo;
+  }
+
+  short8_t qop[KS32], gop[KS32], qnx[KS32], gnx[KS32];
+  float nl = 0.f, del = 0.f, nl_nx = 0.f, del_nx = 0.f;
+  uint32_t mreg = 0;
+  auto load_rows = [&](int n) {
+    const size_t row = (((size_t)b * N + n) * L + ic) * H + h;
+#pragma unroll
+    for (int s = 0; s < KS32; ++s) {
+      const int d0 = 32 * s + 8 * g;
+      short8_t qv = {0, 0, 0, 0, 0, 0, 0, 0}, gv = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (d0 + 8 <= D) {
+        qv = *reinterpret_cast<const short8_t*>(a.q + row * D + d0);
+        gv = *reinterpret_cast<const short8_t*>(a.dout + row * D + d0);
+      } else if (HAS_MASK && AUG_PAD && d0 == D) {
+        qv[0] = (short)a.s_hi;
+        qv[1] = (short)a.s_lo;
+      }
+      qnx[s] = qv;
+      gnx[s] = gv;
+    }
+    const size_t ri = (((size_t)b * N + n) * H + h) * L + ic;
+    nl_nx = a.lse[ri];
+    del_nx = a.delta[ri];
+  };
+  auto load_mask = [&](int n) {
+    if constexpr (HAS_MASK) {
+      if (tid < TL::CH) mreg = a.mask[((size_t)b * N + n) * L + min(tid, L - 1)];
+    }
+  };
+  auto store_mask = [&](int buf) {
+    if constexpr (HAS_MASK) {
+      if (tid < TL::CH) smask[buf][tid] = (uint16_t)mreg;
+    }
+  };
+
+  floatx4 dpacc[WANT_DPAIR ? NB : 1];
+#pragma unroll
+  for (int blk = 0; blk < (WANT_DPAIR ? NB : 1); ++blk) dpacc[blk] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (ntiles > 0) {
+    load_mask(n_begin);
+    issue_kv_tile<D>(smem, a.k, a.v, ((size_t)b * N + n_begin) * L, 0, L, H, h, wave, lane);
+    load_rows(n_begin);
+    store_mask(0);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    const int n = n_begin + t;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < KS32; ++s) {
+      qop[s] = qnx[s];
+      gop[s] = gnx[s];
+    }
+    nl = (nl_nx == kNegInf) ? kNegInf : -nl_nx * kLog2e;  // rows with no finite score: p = 0
+    del = del_nx;
+    if (t + 1 < ntiles) {
+      load_mask(n + 1);
+      issue_kv_tile<D>(smem + ((t + 1) & 1) * TL::BUF_BYTES, a.k, a.v, ((size_t)b * N + n + 1) * L, 0, L, H, h, wave,
+                       lane);
+      load_rows(n + 1);
+    }
+    const uint8_t* kb = smem + (t & 1) * TL::BUF_BYTES;
+    const uint8_t* vb = kb + TL::KCH * 16;
+    const uint16_t* mk = smask[t & 1];
+
+    auto kop = [&](int blk, int s) -> short8_t {
+      const int r = blk * 16 + col;
+      const int c = 4 * s + g;
+      short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (c < TL::KC) {
+        op = *reinterpret_cast<const short8_t*>(kb + (r * TL::KC + (c ^ kv_swz<TL::KC>(r))) * 16);
+      } else if (HAS_MASK && AUG_PAD && c == TL::KC) {
+        const uint16_t m = mk[r];
+        op[0] = (short)m;
+        op[1] = (short)(a.s_lo != 0 ? m : 0);
+      }
+      return op;
+    };
+    auto sblk = [&](int blk) -> floatx4 {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS32; ++s) acc = T::mfma16(kop(blk, s), qop[s], acc);
+      if constexpr (HAS_MASK && !AUG_PAD) {
+        short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (g == 0) {
+          const uint16_t m = mk[blk * 16 + col];
+          op[0] = (short)m;
+          op[1] = (short)(a.s_lo != 0 ? m : 0);
+        }
+        acc = T::mfma16(op, qaug, acc);
+      }
+      return acc;
+    };
+    auto dpblk = [&](int blk) -> floatx4 {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int r = blk * 16 + col;
+#pragma unroll
+      for (int s = 0; s < KS32; ++s) {
+        const int c = 4 * s + g;
+        short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (c < D / 8) op = *reinterpret_cast<const short8_t*>(vb + (r * TL::VC + (c ^ kv_swz<TL::VC>(r))) * 16);
+        acc = T::mfma16(op, gop[s], acc);
+      }
+      return acc;
+    };
+
+    floatx4 dq[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) dq[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 sc[2][2], dp[2][2];
+    sc[0][0] = sblk(0);
+    sc[0][1] = sblk(1);
+    dp[0][0] = dpblk(0);
+    dp[0][1] = dpblk(1);
+#pragma unroll
+    for (int st = 0; st < NB / 2; ++st) {
+      if (32 * st < L) {
+        const int cur = st & 1;
+        // next step's products run under this step's VALU work
+        if (st + 1 < NB / 2 && 32 * (st + 1) < L) {
+          sc[cur ^ 1][0] = sblk(2 * st + 2);
+          sc[cur ^ 1][1] = sblk(2 * st + 3);
+          dp[cur ^ 1][0] = dpblk(2 * st + 2);
+          dp[cur ^ 1][1] = dpblk(2 * st + 3);
+        }
+        // K^T operands of dQ^T for this step (transposed reads, waited on below)
+        short4_t kt[2 * MB];  // [mb][lo/hi]
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int c0 = 16 * mb + 4 * (col & 3);
+          const int r0 = 32 * st + 4 * g + (col >> 2);
+          kt[2 * mb] = lds_read_tr_asm(kb, tr_off<TL::KC>(r0, c0));
+          kt[2 * mb + 1] = lds_read_tr_asm(kb, tr_off<TL::KC>(r0 + 16, c0));
+        }
+        float ds[2][4];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int blk = 2 * st + hb;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float s;
+            if constexpr (HAS_PAIR) {
+              const uint32_t w = pbias[blk][r / 2];
+              s = (r & 1) ? T::fma_mix_hi(sc[cur][hb][r], a.scale, w) : T::fma_mix_lo(sc[cur][hb][r], a.scale, w);
+            } else {
+              s = sc[cur][hb][r] * a.scale;
+            }
+            if (32 * st + 32 > L && 16 * blk + 4 * g + r >= L) s = kNegInf;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s, kLog2e, nl));
+            ds[hb][r] = p * (dp[cur][hb][r] - del);
+          }
+        }
+        const short8_t dsb = __builtin_bit_cast(
+            short8_t, u32x4{T::pack2(ds[0][0], ds[0][1]), T::pack2(ds[0][2], ds[0][3]), T::pack2(ds[1][0], ds[1][1]),
+                            T::pack2(ds[1][2], ds[1][3])});
+        if constexpr (WANT_DPAIR) {
+          dpacc[2 * st] = T::mfma16(sel[0], dsb, dpacc[2 * st]);
+          dpacc[2 * st + 1] = T::mfma16(sel[1], dsb, dpacc[2 * st + 1]);
+        }
+        lds_wait_all(kt);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) dq[mb] = T::mfma16(cat4(kt[2 * mb], kt[2 * mb + 1]), dsb, dq[mb]);
+      }
+    }
+    // ---- dQ = scale * dQ^T: lane holds d = 16 mb + 4 g + 0..3 of query i
+    if (i_valid) {
+      uint16_t* dqrow = a.dq + ((((size_t)b * N + n) * L + i) * H + h) * D;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int d = 16 * mb + 4 * g;
+        if (d < D) {
+          u32x2 w;
+          w[0] = T::pack2(dq[mb][0] * a.scale, dq[mb][1] * a.scale);
+          w[1] = T::pack2(dq[mb][2] * a.scale, dq[mb][3] * a.scale);
+          *reinterpret_cast<u32x2*>(dqrow + d) = w;
+        }
+      }
+    }
+    if (t + 1 < ntiles) store_mask((t + 1) & 1);
+  }
+
+  if constexpr (WANT_DPAIR) {
+    if (i_valid) {
+      float* dst = a.dpair_part + ((((size_t)ng * a.B + b) * H + h) * L + i) * L;
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        const int j = 16 * blk + 4 * g;
+        if (j + 4 <= L && (L % 4) == 0) {
+          *reinterpret_cast<floatx4*>(dst + j) = dpacc[blk];
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (j + u < L) dst[j + u] = dpacc[blk][u];
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- bwd_fin
 
 template <class T>
@@ -556,7 +834,13 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(evo_zero_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dpair_f32, n);
     }
     prof_begin(K_BWD_Q, st);
-    if (!want_dpair) {
+    if (a.L <= KVTile<D>::CH) {
+      const int grid2 = a.B * a.H * ((a.L + kQ2Rows - 1) / kQ2Rows) * a.n_groups_q;
+      if (want_dpair)
+        hipLaunchKernelGGL((evo_bwd_q2_kernel<T, D, HM, HP, true>), dim3(grid2), dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((evo_bwd_q2_kernel<T, D, HM, HP, false>), dim3(grid2), dim3(256), 0, st, a);
+    } else if (!want_dpair) {
       hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, false, 0>), dim3(grid), dim3(256), 0, st, a);
     } else if (nchunks <= 2) {
       hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, true, 2>), dim3(grid), dim3(256), 0, st, a);

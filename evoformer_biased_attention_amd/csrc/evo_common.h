@@ -6,6 +6,10 @@
 //   B operand (16 x 32): lane l holds B[8*(l/32) + e][l % 32]
 //   C/D       (32 x 32): lane l, register r holds C[8*(r/4) + 4*(l/32) + r%4][l % 32]
 // so a lane always owns one output column and 16 rows in four runs of four.
+// v_mfma_f32_16x16x32_{f16,bf16}:
+//   A (16 x 32): lane l holds A[l % 16][8*(l/16) + e]
+//   B (32 x 16): lane l holds B[8*(l/16) + e][l % 16]
+//   C (16 x 16): lane l, register r holds C[4*(l/16) + r][l % 16]
 //
 // ds_read_b64_tr_b16, per group of 16 lanes: lane i supplies the address of
 // four consecutive 16-bit elements M[i][0..3]; lane j receives
@@ -52,9 +56,32 @@ struct F16 {
   static __device__ __forceinline__ floatx16 mfma(const short8_t& a, const short8_t& b, const floatx16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
   }
+  static __device__ __forceinline__ floatx4 mfma16(const short8_t& a, const short8_t& b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ short one() { return (short)0x3c00; }
   // mixed fma: a*b + (float)h, h a stored 16-bit value
   static __device__ __forceinline__ float fma_mix(float a, float b, uint16_t h) {
     return __builtin_fmaf(a, b, (float)__builtin_bit_cast(_Float16, h));
+  }
+  // a*b + half of a packed pair, in one v_fma_mix_f32 (the compiler does not
+  // form it from a packed register on its own)
+  static __device__ __forceinline__ float fma_mix_lo(float a, float b, uint32_t w) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,0,1]" : "=v"(r) : "v"(a), "v"(b), "v"(w));
+    return r;
+  }
+  static __device__ __forceinline__ float fma_mix_hi(float a, float b, uint32_t w) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "=v"(r) : "v"(a), "v"(b), "v"(w));
+    return r;
+  }
+  // running row sum of the probabilities: fp16 sums the rounded pair in one
+  // v_dot2_f32_f16 (fp32 accumulation; the rounding is 2^-11 relative)
+  static __device__ __forceinline__ float rowsum_add(float acc, float, float, uint32_t packed) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, packed), one, acc, false);
   }
 };
 
@@ -73,8 +100,22 @@ struct BF16 {
   static __device__ __forceinline__ floatx16 mfma(const short8_t& a, const short8_t& b, const floatx16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   }
+  static __device__ __forceinline__ floatx4 mfma16(const short8_t& a, const short8_t& b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ short one() { return (short)0x3f80; }
   static __device__ __forceinline__ float fma_mix(float a, float b, uint16_t h) {
     return __builtin_fmaf(a, b, to_f32(h));
+  }
+  static __device__ __forceinline__ float fma_mix_lo(float a, float b, uint32_t w) {
+    return __builtin_fmaf(a, b, __builtin_bit_cast(float, w << 16));
+  }
+  static __device__ __forceinline__ float fma_mix_hi(float a, float b, uint32_t w) {
+    return __builtin_fmaf(a, b, __builtin_bit_cast(float, w & 0xffff0000u));
+  }
+  // bf16 rounding (2^-8) is too coarse for the lse: sum the fp32 values
+  static __device__ __forceinline__ float rowsum_add(float acc, float p0, float p1, uint32_t) {
+    return acc + (p0 + p1);
   }
 };
 
@@ -88,6 +129,13 @@ __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u,
 // pads cover the VALU-write -> permlane-read hazard on either side.
 __device__ __forceinline__ void xhalf_swap(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+// The value lane l ^ 32 holds.
+__device__ __forceinline__ uint32_t xhalf_partner(uint32_t x) {
+  float a = __builtin_bit_cast(float, x), b = a;
+  xhalf_swap(a, b);  // lanes < 32 find the partner's value in b, lanes >= 32 in a
+  const bool lo = (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) < 32);
+  return __builtin_bit_cast(uint32_t, lo ? b : a);
 }
 __device__ __forceinline__ float xhalf_max(float x) {
   float a = x, b = x;
@@ -109,6 +157,108 @@ __device__ __forceinline__ short4_t lds_read_tr(const uint16_t* lds_base, int el
 __device__ __forceinline__ short8_t cat4(short4_t a, short4_t b) {
   short8_t r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return r;
+}
+
+// ------------------------------------------------------- K/V tiles in LDS
+//
+// A tile holds CH keys of one (b, n, h): K rows of D elements, then V rows
+// padded to at least 32 elements (the transposed reads of V^T touch 32
+// columns; the padding is never used).  Both are filled by
+// global_load_lds_dwordx4, which writes 64 consecutive 16-byte chunks per wave
+// instruction, so the layout is a dense array of 16-byte chunks.  Chunk c of
+// row r sits at position c ^ swz(r): 16 consecutive rows read at the same
+// column then hit 16 distinct 4-bank groups.
+template <int C>
+__device__ __forceinline__ int kv_swz(int r) {
+  constexpr int R = 16 / C;  // rows per 64-dword bank cycle
+  return (r / R) % C;
+}
+
+template <int D>
+struct KVTile {
+  static constexpr int CH = (D == 64) ? 128 : 256;  // keys per tile
+  static constexpr int KC = D / 8;                  // 16-byte chunks per K row
+  static constexpr int VC = (D < 32 ? 32 : D) / 8;  // 16-byte chunks per V row
+  static constexpr int KCH = CH * KC;
+  static constexpr int VCH = CH * VC;
+  static constexpr int TCH = KCH + VCH;             // chunks per tile (a multiple of 256)
+  static constexpr int BUF_BYTES = TCH * 16;
+  static_assert(TCH % 256 == 0, "tile must split evenly over 256 threads");
+};
+
+// Issue the asynchronous copy of keys [kc0, kc0 + CH) of one (b, n, h) slice
+// (K rows then V rows, swizzled) into an LDS tile buffer.  Every thread of a
+// 256-thread workgroup takes part; keys past L copy key L-1 (never used).
+template <int D>
+__device__ __forceinline__ void issue_kv_tile(uint8_t* buf, const uint16_t* k, const uint16_t* v, size_t slice_row,
+                                              int kc0, int L, int H, int h, int wave, int lane) {
+  using TL = KVTile<D>;
+  for (int base = wave * 64; base < TL::TCH; base += 256) {
+    const int q = base + lane;
+    const uint16_t* src;
+    if (q < TL::KCH) {
+      const int r = q / TL::KC, pos = q % TL::KC;
+      const int c = pos ^ kv_swz<TL::KC>(r);
+      const int j = min(kc0 + r, L - 1);
+      src = k + ((slice_row + j) * H + h) * D + 8 * c;
+    } else {
+      const int q2 = q - TL::KCH;
+      const int r = q2 / TL::VC, pos = q2 % TL::VC;
+      int c = pos ^ kv_swz<TL::VC>(r);
+      if (c >= D / 8) c = 0;  // columns the transposed reads touch but never use
+      const int j = min(kc0 + r, L - 1);
+      src = v + ((slice_row + j) * H + h) * D + 8 * c;
+    }
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(buf + base * 16), 16, 0, 0);
+  }
+}
+
+// byte offset of element (row, col) in a swizzled tile with C chunks per row
+template <int C>
+__device__ __forceinline__ int tr_off(int row, int col) {
+  return (row * C + ((col >> 3) ^ kv_swz<C>(row))) * 16 + (col & 7) * 2;
+}
+
+__device__ __forceinline__ short4_t lds_read_tr_b(const uint8_t* base, int byte_off) {
+  const __attribute__((address_space(3))) uint8_t* p = (const __attribute__((address_space(3))) uint8_t*)base + byte_off;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
+}
+
+// The same transposed read as inline assembly.  The compiler treats the
+// builtin as possibly aliasing every LDS copy still in flight from
+// global_load_lds and waits for all of them (vmcnt(0)) before it, which
+// would stall on the next tile's prefetch.  Reads issued this way are not
+// tracked by the compiler: call lds_wait() before using their results.
+// Buffers being filled by global_load_lds are never read this way before the
+// s_waitcnt + barrier that completes them.
+__device__ __forceinline__ short4_t lds_read_tr_asm(const uint8_t* base, int byte_off) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const uint32_t addr = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint8_t*)base + byte_off);
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return __builtin_bit_cast(short4_t, r);
+}
+// Wait for the reads above and make the waited registers outputs of the wait,
+// so that no consumer can be scheduled before it.
+__device__ __forceinline__ void lds_wait(short4_t& a, short4_t& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b)::"memory");
+}
+__device__ __forceinline__ void lds_wait(short4_t& a, short4_t& b, short4_t& c, short4_t& d) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d)::"memory");
+}
+template <int N>
+__device__ __forceinline__ void lds_wait_all(short4_t (&r)[N]) {
+  static_assert(N % 2 == 0, "pairs");
+  if constexpr (N == 2) {
+    lds_wait(r[0], r[1]);
+  } else if constexpr (N == 4) {
+    lds_wait(r[0], r[1], r[2], r[3]);
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < N; ++k) asm volatile("" : "+v"(r[k]));
+  }
 }
 
 // Row stride (in 16-bit elements) for an LDS tile whose rows are read 16 bytes

@@ -32,7 +32,6 @@ namespace evo {
 
 constexpr int kFwdWaves = 4;
 constexpr int kFwdRows = 32 * kFwdWaves;  // query rows per workgroup
-constexpr int kFwdChunk = 128;            // keys staged in LDS at a time
 constexpr float kTauNat = 5.545177444479562f;  // 8 * ln 2
 
 template <int D, bool HAS_MASK>
@@ -66,22 +65,23 @@ __device__ __forceinline__ short8_t load_q8(const uint16_t* row, int c, bool val
 
 // Pair-bias values for one 32-key block in the S^T accumulator layout:
 // lane (query i) gets pair[i][j0 + 8q + 4*(l/32) + u], q,u = 0..3, packed two per dword.
-__device__ __forceinline__ void load_pair_block(u32x2 (&dst)[4], const uint16_t* prow, int i_valid, int j0, int L,
-                                                int half, bool vec_ok) {
+// Branch-free: rows and columns are clamped into range and the values of
+// columns >= L are replaced by zero (those keys are masked to -inf later).
+__device__ __forceinline__ void load_pair_block(u32x2 (&dst)[4], const uint16_t* prow, int j0, int L, int half,
+                                                bool vec_ok) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    int j = j0 + 8 * q + 4 * half;
-    u32x2 v = {0u, 0u};
-    if (i_valid) {
-      if (vec_ok && j + 4 <= L) {
-        v = *reinterpret_cast<const u32x2*>(prow + j);
-      } else {
-        uint16_t t[4];
+    const int j = j0 + 8 * q + 4 * half;
+    u32x2 v;
+    if (vec_ok) {  // uniform: L % 4 == 0, so j + 3 < L whenever j < L
+      v = *reinterpret_cast<const u32x2*>(prow + min(j, L - 4));
+      if (j >= L) v = u32x2{0u, 0u};
+    } else {
+      uint32_t t[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) t[u] = (j + u < L) ? prow[j + u] : (uint16_t)0;
-        v[0] = (uint32_t)t[0] | ((uint32_t)t[1] << 16);
-        v[1] = (uint32_t)t[2] | ((uint32_t)t[3] << 16);
-      }
+      for (int u = 0; u < 4; ++u) t[u] = (j + u < L) ? (uint32_t)prow[min(j + u, L - 1)] : 0u;
+      v[0] = t[0] | (t[1] << 16);
+      v[1] = t[2] | (t[3] << 16);
     }
     dst[q] = v;
   }
@@ -95,8 +95,12 @@ __device__ __forceinline__ uint16_t pick16(const u32x2 (&b)[4], int r) {
 template <class T, int D, bool HAS_MASK, bool HAS_PAIR, int RES>
 __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   using S = FwdShape<D, HAS_MASK>;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kFwdChunk * S::KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kFwdChunk * S::VS];
+  using TL = KVTile<D>;
+  // two K/V tile buffers; with a resident pair bias the same bytes first hold
+  // the workgroup's 128 x (32 RES) bias slab
+  constexpr int kSlab = RES > 0 ? kFwdRows * RES * 64 : 0;
+  constexpr int kSmem = 2 * TL::BUF_BYTES > kSlab ? 2 * TL::BUF_BYTES : kSlab;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,199 +108,335 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   const int half = lane >> 5;
   const int L = a.L, H = a.H, N = a.N;
 
-  // workgroup -> (b, h, i-tile, n-group); consecutive ids of one XCD share (b, h, i-tile)
+  // workgroup -> (h, i-tile, n-group, b) with h fastest: the ids one XCD gets
+  // are consecutive, so all heads and query tiles of a run of slices share
+  // that XCD's L2 (the heads of a row are interleaved in memory)
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int ng = wg % a.n_groups;
-  int rest = wg / a.n_groups;
+  const int h = wg % H;
+  int rest = wg / H;
   const int it = rest % a.i_tiles;
   rest /= a.i_tiles;
-  const int h = rest % H;
-  const int b = rest / H;
+  const int ng = rest % a.n_groups;
+  const int b = rest / a.n_groups;
 
   const int i = it * kFwdRows + wave * 32 + (lane & 31);
   const bool i_valid = i < L;
+  const int ic = min(i, L - 1);  // rows past L compute a copy of row L-1 and are not stored
   const int n_begin = ng * a.G;
   const int n_end = min(N, n_begin + a.G);
-  const int nkb = (L + 31) / 32;  // key blocks
+  const int nchunks = (L + TL::CH - 1) / TL::CH;
+  const int ntiles = (n_end - n_begin) * nchunks;
 
-  // ---- pair-bias registers (loaded once when the whole row fits)
+  // ---- pair-bias registers (loaded once when the whole row fits one tile)
   u32x2 pres[RES > 0 ? RES : 1][4];
   const uint16_t* prow = nullptr;
   const bool pvec = (L % 4) == 0;
   if constexpr (HAS_PAIR) {
-    prow = a.pair + (((size_t)b * H + h) * L + (i_valid ? i : 0)) * L;
+    prow = a.pair + (((size_t)b * H + h) * L + ic) * L;
     if constexpr (RES > 0) {
+      if ((L % 8) == 0) {
+        // Coalesced: the workgroup's 128 rows x L pair-bias slab goes to LDS by
+        // asynchronous 16-byte copies (chunk c of row r stored at position
+        // c ^ (r & 15), so the per-lane reads below are spread over the banks),
+        // then every lane picks its values.  Runs before the first K/V tile.
+        constexpr int RC = RES * 4;  // 16-byte chunks per staged row
+        const uint16_t* pbase = a.pair + ((size_t)b * H + h) * L * L;
+        const int row0 = it * kFwdRows;
+        for (int base = wave * 64; base < kFwdRows * RC; base += 256) {
+          const int q = base + lane;
+          const int r = q / RC, pos = q % RC;
+          const int c = min(pos ^ (r & 15), L / 8 - 1);
+          const uint16_t* src = pbase + (size_t)min(row0 + r, L - 1) * L + 8 * c;
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                           (__attribute__((address_space(3))) void*)(smem + base * 16), 16, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const int r = wave * 32 + (lane & 31);
 #pragma unroll
-      for (int kb = 0; kb < RES; ++kb) {
-        if (kb < nkb) load_pair_block(pres[kb], prow, i_valid, kb * 32, L, half, pvec);
+        for (int kb = 0; kb < RES; ++kb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = 4 * kb + q;  // chunk holding keys 32 kb + 8 q .. +7
+            pres[kb][q] = *reinterpret_cast<const u32x2*>(smem + (r * RC + ((c ^ (r & 15)) % RC)) * 16 + 8 * half);
+          }
+        __syncthreads();  // the slab area is reused by the K/V tiles
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < RES; ++kb) load_pair_block(pres[kb], prow, kb * 32, L, half, pvec);
       }
     }
   }
 
-  for (int n = n_begin; n < n_end; ++n) {
-    const size_t slice = ((size_t)b * N + n) * L;  // row index of (b, n, 0)
-    // ---- Q operand (B of S^T = K Q^T): lane owns query i, 8 columns per k-step
-    short8_t qop[S::KSTEPS];
-    {
-      const uint16_t* qrow = a.q + ((slice + (i_valid ? i : 0)) * H + h) * D;
-#pragma unroll
-      for (int s = 0; s < S::KSTEPS; ++s)
-        qop[s] = load_q8<D>(qrow, 16 * s + 8 * half, i_valid, a.s_hi, a.s_lo, HAS_MASK);
-    }
-    floatx16 oacc[S::MB];
-#pragma unroll
-    for (int mb = 0; mb < S::MB; ++mb) oacc[mb] = floatx16{};
-    float m_used = kNegInf;
-    float l_part = 0.f;
+  // constant mask-augmentation operand of Q: {s_hi, s_lo} in the k-slots after D
+  short8_t qaug = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (HAS_MASK && half == 0) {
+    qaug[0] = (short)a.s_hi;
+    qaug[1] = (short)a.s_lo;
+  }
 
-    // ---- stage K (with mask columns) and V rows [kc0, kc0 + chunk) of slice n
-    auto stage = [&](const int kc0, const size_t slice_, const int n_) {
-      constexpr int V8 = D / 8;  // 16-byte pieces per row
-      for (int t = tid; t < kFwdChunk * V8; t += 256) {
-        int r = t / V8, c8 = t % V8;
-        int j = kc0 + r;
-        short8_t kv = {0, 0, 0, 0, 0, 0, 0, 0}, vv = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (j < L) {
-          size_t off = ((slice_ + j) * H + h) * D + c8 * 8;
-          kv = *reinterpret_cast<const short8_t*>(a.k + off);
-          vv = *reinterpret_cast<const short8_t*>(a.v + off);
-        }
-        *reinterpret_cast<short8_t*>(&sK[r * S::KS + c8 * 8]) = kv;
-        *reinterpret_cast<short8_t*>(&sV[r * S::VS + c8 * 8]) = vv;
-      }
-      if constexpr (S::KW > D) {
-        for (int r = tid; r < kFwdChunk; r += 256) {
-          int j = kc0 + r;
-          uint16_t m = 0;
-          if constexpr (HAS_MASK) m = (j < L) ? a.mask[((size_t)b * N + n_) * L + j] : (uint16_t)0;
-          for (int c = D; c < S::KW; ++c) {
-            uint16_t val = 0;
-            if (HAS_MASK && c == D) val = m;
-            if (HAS_MASK && c == D + 1 && a.s_lo != 0) val = m;
-            sK[r * S::KS + c] = val;
-          }
-        }
-      }
-    };
+  short8_t qop[S::KSTEPS_D], qnext[S::KSTEPS_D];
+  // mask values (one per dword so that a prefetched value is never repacked,
+  // which would force an early wait on the loads still in flight)
+  uint32_t mcur[TL::CH / 32], mnext[TL::CH / 32];
 
-    // ---- one 32-key block: scores, online softmax, PV
-    auto block = [&](const int jb, const int j0, const u32x2 (&pb)[4]) {
-      floatx16 acc = floatx16{};
+  auto load_q = [&](short8_t (&dst)[S::KSTEPS_D], int n) {
+    const size_t slice = ((size_t)b * N + n) * L;
+    const uint16_t* qrow = a.q + ((slice + ic) * H + h) * D;
 #pragma unroll
-      for (int s = 0; s < S::KSTEPS; ++s) {
-        short8_t kop = *reinterpret_cast<const short8_t*>(&sK[(jb * 32 + (lane & 31)) * S::KS + 16 * s + 8 * half]);
-        acc = T::mfma(kop, qop[s], acc);
-      }
-      float sv[16];
-      if constexpr (HAS_PAIR) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sv[r] = T::fma_mix(acc[r], a.scale, pick16(pb, r));
+    for (int s = 0; s < S::KSTEPS_D; ++s) {
+      const int c = 16 * s + 8 * half;
+      short8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (c + 8 <= D) {
+        v = *reinterpret_cast<const short8_t*>(qrow + c);
       } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sv[r] = acc[r] * a.scale;
-      }
-      if (j0 + 32 > L) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int j = j0 + 8 * (r / 4) + 4 * half + (r % 4);
-          if (j >= L) sv[r] = kNegInf;
+        v = qaug;  // D = 8: the upper k-slots carry the mask augmentation (or zeros)
+        if (HAS_MASK) {
+          v[0] = (short)a.s_hi;
+          v[1] = (short)a.s_lo;
         }
       }
-      float mb = sv[0];
+      dst[s] = v;
+    }
+  };
+  // keys past L read the mask of key L-1; their scores are forced to -inf anyway
+  auto load_mask = [&](uint32_t (&dst)[TL::CH / 32], int n, int kc0) {
+    if constexpr (HAS_MASK) {
+      const uint16_t* mrow = a.mask + ((size_t)b * N + n) * L;
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mb = __builtin_fmaxf(mb, sv[r]);
-      mb = xhalf_max(mb);
-      const bool need = mb > m_used + kTauNat;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        float m_new = need ? mb : m_used;
-        float alpha = need ? __builtin_amdgcn_exp2f((m_used - m_new) * kLog2e) : 1.f;
-        m_used = m_new;
-        l_part *= alpha;
-#pragma unroll
-        for (int mb2 = 0; mb2 < S::MB; ++mb2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[mb2][r] *= alpha;
+      for (int jb = 0; jb < TL::CH / 32; ++jb) dst[jb] = mrow[min(kc0 + jb * 32 + (lane & 31), L - 1)];
+    }
+  };
+  // issue the asynchronous copy of tile t into LDS buffer (t & 1)
+  auto issue_tile = [&](int t) {
+    const int n = n_begin + t / nchunks;
+    const int kc0 = (t % nchunks) * TL::CH;
+    const size_t slice = ((size_t)b * N + n) * L;
+    uint8_t* buf = smem + (t & 1) * TL::BUF_BYTES;
+    for (int base = wave * 64; base < TL::TCH; base += 256) {
+      const int q = base + lane;
+      const uint16_t* src;
+      if (q < TL::KCH) {
+        const int r = q / TL::KC, pos = q % TL::KC;
+        const int c = pos ^ kv_swz<TL::KC>(r);
+        const int j = min(kc0 + r, L - 1);
+        src = a.k + ((slice + j) * H + h) * D + 8 * c;
+      } else {
+        const int q2 = q - TL::KCH;
+        const int r = q2 / TL::VC, pos = q2 % TL::VC;
+        int c = pos ^ kv_swz<TL::VC>(r);
+        if (c >= D / 8) c = 0;  // columns the transposed reads touch but never use
+        const int j = min(kc0 + r, L - 1);
+        src = a.v + ((slice + j) * H + h) * D + 8 * c;
       }
-      const float neg_ml = (m_used == kNegInf) ? 0.f : -m_used * kLog2e;
-      uint32_t pk[8];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], kLog2e, neg_ml));
-        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + 1], kLog2e, neg_ml));
-        l_part += p0 + p1;
-        pk[r / 2] = T::pack2(p0, p1);
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        short8_t bop = __builtin_bit_cast(short8_t, u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]});
-        const int qg = lane >> 4, i16 = lane & 15;
-        const int g = qg >> 1;
-        const int k0 = jb * 32 + 16 * t + 4 * g;
-#pragma unroll
-        for (int mb2 = 0; mb2 < S::MB; ++mb2) {
-          const int n0 = 16 * (qg & 1) + 32 * mb2;
-          const int e1 = (k0 + (i16 >> 2)) * S::VS + n0 + 4 * (i16 & 3);
-          const int e2 = e1 + 8 * S::VS;
-          short8_t aop = cat4(lds_read_tr(sV, e1), lds_read_tr(sV, e2));
-          oacc[mb2] = T::mfma(aop, bop, oacc[mb2]);
-        }
-      }
-    };
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(buf + base * 16), 16, 0, 0);
+    }
+  };
 
-    const int nchunks = (L + kFwdChunk - 1) / kFwdChunk;
-    if constexpr (RES > 0) {
-      // L <= 32*RES: the chunk and block loops are unrolled so that the
-      // resident pair-bias block is selected at compile time.
-      constexpr int kChunksRes = (RES * 32 + kFwdChunk - 1) / kFwdChunk;
+  floatx16 oacc[S::MB];
+  float m_used = kNegInf, l_part = 0.f;
+
+  // ---- S^T block = K Q^T for 32 keys of tile buffer `buf` (mask via the extra k-step)
+  auto qk_block = [&](const uint8_t* buf, const int jb, const uint32_t mj) -> floatx16 {
+    floatx16 acc = floatx16{};
+    const int r = jb * 32 + (lane & 31);
+    short8_t kop[S::KSTEPS_D];
 #pragma unroll
-      for (int c = 0; c < kChunksRes; ++c) {
-        if (c < nchunks) {
-          const int kc0 = c * kFwdChunk;
-          __syncthreads();  // previous chunk fully consumed
-          stage(kc0, slice, n);
-          __syncthreads();
-#pragma unroll
-          for (int jb = 0; jb < kFwdChunk / 32; ++jb) {
-            const int kb = c * (kFwdChunk / 32) + jb;
-            if (kb < RES && kc0 + jb * 32 < L) block(jb, kc0 + jb * 32, pres[kb < RES ? kb : 0]);
-          }
+    for (int s = 0; s < S::KSTEPS_D; ++s) {
+      const int c = 2 * s + half;
+      if (c < TL::KC) {
+        kop[s] = *reinterpret_cast<const short8_t*>(buf + (r * TL::KC + (c ^ kv_swz<TL::KC>(r))) * 16);
+      } else {  // D = 8, upper k-slots: mask augmentation (or zeros)
+        kop[s] = short8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        if (HAS_MASK) {
+          kop[s][0] = (short)mj;
+          kop[s][1] = (short)(a.s_lo != 0 ? mj : 0);
         }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS_D; ++s) acc = T::mfma(kop[s], qop[s], acc);
+    if constexpr (HAS_MASK && (D % 16) == 0) {
+      short8_t ka = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (half == 0) {
+        ka[0] = (short)mj;
+        ka[1] = (short)(a.s_lo != 0 ? mj : 0);
+      }
+      acc = T::mfma(ka, qaug, acc);
+    }
+    return acc;
+  };
+
+  // ---- bias, online softmax and O^T += V^T P^T for one block whose scores are in acc
+  auto softmax_pv = [&](const floatx16& acc, const uint8_t* buf, const int jb, const int j0, const u32x2 (&pb)[4]) {
+    const uint8_t* vb = buf + TL::KCH * 16;
+    // V^T operands first: the reads complete under the softmax VALU work
+    const int qg = lane >> 4, i16 = lane & 15, g = qg >> 1;
+    short4_t vt[4 * S::MB];  // [t][mb][lo/hi]
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = jb * 32 + 16 * t + 4 * g + (i16 >> 2);
+#pragma unroll
+      for (int mb2 = 0; mb2 < S::MB; ++mb2) {
+        const int col = 16 * (qg & 1) + 32 * mb2 + 4 * (i16 & 3);
+        vt[(t * S::MB + mb2) * 2 + 0] = lds_read_tr_asm(vb, tr_off<TL::VC>(row, col));
+        vt[(t * S::MB + mb2) * 2 + 1] = lds_read_tr_asm(vb, tr_off<TL::VC>(row + 8, col));
+      }
+    }
+    float sv[16];
+    if constexpr (HAS_PAIR) {
+#pragma unroll
+      for (int rr = 0; rr < 16; rr += 2) {
+        const uint32_t w = pb[rr / 4][(rr % 4) / 2];
+        sv[rr] = T::fma_mix_lo(acc[rr], a.scale, w);
+        sv[rr + 1] = T::fma_mix_hi(acc[rr + 1], a.scale, w);
       }
     } else {
-      for (int c = 0; c < nchunks; ++c) {
-        const int kc0 = c * kFwdChunk;
-        __syncthreads();
-        stage(kc0, slice, n);
-        __syncthreads();
-        const int nblk = (min(kFwdChunk, L - kc0) + 31) / 32;
-        for (int jb = 0; jb < nblk; ++jb) {
-          u32x2 pb[4] = {};
-          if constexpr (HAS_PAIR) load_pair_block(pb, prow, i_valid, kc0 + jb * 32, L, half, pvec);
-          block(jb, kc0 + jb * 32, pb);
-        }
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sv[rr] = acc[rr] * a.scale;
+    }
+    if (j0 + 32 > L) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int j = j0 + 8 * (rr / 4) + 4 * half + (rr % 4);
+        if (j >= L) sv[rr] = kNegInf;
       }
     }
-
-    // ---- epilogue: normalise, store O and lse
-    const float l_tot = xhalf_sum(l_part);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (i_valid) {
-      uint16_t* orow = a.out + ((slice + i) * H + h) * D;
+    float mb = sv[0];
+#pragma unroll
+    for (int rr = 1; rr < 16; ++rr) mb = __builtin_fmaxf(mb, sv[rr]);
+    mb = xhalf_max(mb);
+    const bool need = mb > m_used + kTauNat;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = need ? mb : m_used;
+      const float alpha = need ? __builtin_amdgcn_exp2f((m_used - m_new) * kLog2e) : 1.f;
+      m_used = m_new;
+      l_part *= alpha;
 #pragma unroll
       for (int mb2 = 0; mb2 < S::MB; ++mb2)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int d = 32 * mb2 + 8 * q + 4 * half;
-          if (d < D) {
-            u32x2 w;
-            w[0] = T::pack2(oacc[mb2][4 * q] * inv, oacc[mb2][4 * q + 1] * inv);
-            w[1] = T::pack2(oacc[mb2][4 * q + 2] * inv, oacc[mb2][4 * q + 3] * inv);
-            *reinterpret_cast<u32x2*>(orow + d) = w;
-          }
+        for (int rr = 0; rr < 16; ++rr) oacc[mb2][rr] *= alpha;
+    }
+    const float neg_ml = (m_used == kNegInf) ? 0.f : -m_used * kLog2e;
+    uint32_t pk[8];
+#pragma unroll
+    for (int rr = 0; rr < 16; rr += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr], kLog2e, neg_ml));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr + 1], kLog2e, neg_ml));
+      pk[rr / 2] = T::pack2(p0, p1);
+      l_part = T::rowsum_add(l_part, p0, p1, pk[rr / 2]);
+    }
+    lds_wait_all(vt);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const short8_t bop = __builtin_bit_cast(short8_t, u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]});
+#pragma unroll
+      for (int mb2 = 0; mb2 < S::MB; ++mb2)
+        oacc[mb2] = T::mfma(cat4(vt[(t * S::MB + mb2) * 2], vt[(t * S::MB + mb2) * 2 + 1]), bop, oacc[mb2]);
+    }
+  };
+
+  // ---- pipeline: tile t computes from buffer t&1 while tile t+1 streams into the other
+  if (ntiles > 0) {
+    issue_tile(0);
+    load_mask(mnext, n_begin, 0);
+    load_q(qnext, n_begin);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    const int n = n_begin + t / nchunks;
+    const int c = t % nchunks;
+    const int kc0 = c * TL::CH;
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's copies of tile t (and its mask/Q loads) are done
+    __syncthreads();                // everyone's are; everyone has finished tile t-1
+#pragma unroll
+    for (int jb = 0; jb < TL::CH / 32; ++jb) mcur[jb] = mnext[jb];
+    if (c == 0) {
+#pragma unroll
+      for (int s = 0; s < S::KSTEPS_D; ++s) qop[s] = qnext[s];
+#pragma unroll
+      for (int mb2 = 0; mb2 < S::MB; ++mb2) oacc[mb2] = floatx16{};
+      m_used = kNegInf;
+      l_part = 0.f;
+    }
+    // streamed pair bias: this tile's blocks are loaded before the next tile's
+    // copies are issued, so waiting for them never waits for the prefetch
+    u32x2 ptile[RES > 0 || !HAS_PAIR ? 1 : TL::CH / 32][4];
+    if constexpr (RES == 0 && HAS_PAIR) {
+#pragma unroll
+      for (int jb = 0; jb < TL::CH / 32; ++jb) load_pair_block(ptile[jb], prow, kc0 + jb * 32, L, half, pvec);
+    }
+    if (t + 1 < ntiles) {
+      issue_tile(t + 1);
+      const int n1 = n_begin + (t + 1) / nchunks;
+      load_mask(mnext, n1, ((t + 1) % nchunks) * TL::CH);
+      if ((t + 1) % nchunks == 0) load_q(qnext, n1);
+    }
+    const uint8_t* buf = smem + (t & 1) * TL::BUF_BYTES;
+    // blocks of the tile, software-pipelined: the QK^T MFMAs of block jb+1 are
+    // issued before the softmax of block jb so that they run under its VALU work
+    const int nblk = min(TL::CH, L - kc0 + 31) / 32;
+    if constexpr (RES > 0) {
+      // the whole row is one tile: blocks unrolled so the resident bias is indexed statically
+      constexpr int NB = RES < TL::CH / 32 ? RES : TL::CH / 32;
+      floatx16 sacc[2];
+      sacc[0] = qk_block(buf, 0, mcur[0]);
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) {
+        if (jb < nblk) {
+          if (jb + 1 < NB && jb + 1 < nblk) sacc[(jb + 1) & 1] = qk_block(buf, jb + 1, mcur[jb + 1]);
+          softmax_pv(sacc[jb & 1], buf, jb, jb * 32, pres[jb]);
         }
-      if (half == 0) {
-        float lse = (m_used == kNegInf || !(l_tot > 0.f)) ? kNegInf : m_used + __logf(l_tot);
-        a.lse[(((size_t)b * N + n) * H + h) * L + i] = lse;
+      }
+    } else {
+      floatx16 sacc[2];
+      sacc[0] = qk_block(buf, 0, mcur[0]);
+#pragma unroll
+      for (int jb = 0; jb < TL::CH / 32; ++jb) {
+        if (jb < nblk) {
+          if (jb + 1 < TL::CH / 32 && jb + 1 < nblk) sacc[(jb + 1) & 1] = qk_block(buf, jb + 1, mcur[jb + 1]);
+          softmax_pv(sacc[jb & 1], buf, jb, kc0 + jb * 32, ptile[HAS_PAIR ? jb : 0]);
+        }
+      }
+    }
+    if (c == nchunks - 1) {
+      // ---- epilogue of slice n: normalise, store O and lse
+      const size_t slice = ((size_t)b * N + n) * L;
+      const float l_tot = xhalf_sum(l_part);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      {
+        // lanes l and l^32 hold alternating runs of 4 columns of the same row;
+        // one exchange per pair of runs gives each lane 8 contiguous columns,
+        // stored as one 16-byte write
+        uint16_t* orow = a.out + ((slice + ic) * H + h) * D;
+#pragma unroll
+        for (int mb2 = 0; mb2 < S::MB; ++mb2)
+#pragma unroll
+          for (int q = 0; q < 4; q += 2) {
+            uint32_t run[2][2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              run[u][0] = T::pack2(oacc[mb2][4 * (q + u)] * inv, oacc[mb2][4 * (q + u) + 1] * inv);
+              run[u][1] = T::pack2(oacc[mb2][4 * (q + u) + 2] * inv, oacc[mb2][4 * (q + u) + 3] * inv);
+            }
+            // half 0 keeps run q and receives the partner's run q; half 1 keeps
+            // run q+1 and receives the partner's run q+1
+            uint32_t snd0 = half ? run[0][0] : run[1][0];
+            uint32_t snd1 = half ? run[0][1] : run[1][1];
+            const uint32_t rcv0 = xhalf_partner(snd0), rcv1 = xhalf_partner(snd1);
+            u32x4 w;
+            if (half == 0) {
+              w = u32x4{run[0][0], run[0][1], rcv0, rcv1};
+            } else {
+              w = u32x4{rcv0, rcv1, run[1][0], run[1][1]};
+            }
+            const int d = 32 * mb2 + 8 * (q + half);
+            if (i_valid && d < D) *reinterpret_cast<u32x4*>(orow + d) = w;
+          }
+        if (i_valid && half == 0) {
+          const float lse = (m_used == kNegInf || !(l_tot > 0.f)) ? kNegInf : m_used + __logf(l_tot);
+          a.lse[(((size_t)b * N + n) * H + h) * L + i] = lse;
+        }
       }
     }
   }
@@ -308,8 +448,8 @@ template <class T, int D, bool HM, bool HP>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int grid = a.B * a.H * a.i_tiles * a.n_groups;
   prof_begin(K_FWD, stream);
-  if (HP && a.L <= 256) {
-    hipLaunchKernelGGL((evo_fwd_kernel<T, D, HM, HP, 8>), dim3(grid), dim3(256), 0, stream, a);
+  if (HP && a.L <= KVTile<D>::CH) {
+    hipLaunchKernelGGL((evo_fwd_kernel<T, D, HM, HP, KVTile<D>::CH / 32>), dim3(grid), dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL((evo_fwd_kernel<T, D, HM, HP, 0>), dim3(grid), dim3(256), 0, stream, a);
   }
