@@ -60,6 +60,7 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ short one() { return (short)0x3c00; }
+  static constexpr uint16_t kNegInfBits = 0xfc00;
   // mixed fma: a*b + (float)h, h a stored 16-bit value
   static __device__ __forceinline__ float fma_mix(float a, float b, uint16_t h) {
     return __builtin_fmaf(a, b, (float)__builtin_bit_cast(_Float16, h));
@@ -104,6 +105,7 @@ struct BF16 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ short one() { return (short)0x3f80; }
+  static constexpr uint16_t kNegInfBits = 0xff80;
   static __device__ __forceinline__ float fma_mix(float a, float b, uint16_t h) {
     return __builtin_fmaf(a, b, to_f32(h));
   }
@@ -239,6 +241,14 @@ __device__ __forceinline__ short4_t lds_read_tr_asm(const uint8_t* base, int byt
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
   return __builtin_bit_cast(short4_t, r);
 }
+// A 16-byte LDS read in the same style (not tracked by the compiler).
+__device__ __forceinline__ short8_t lds_read_b128_asm(const uint8_t* base, int byte_off) {
+  const uint32_t addr = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint8_t*)base + byte_off);
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+  return __builtin_bit_cast(short8_t, r);
+}
+
 // Wait for the reads above and make the waited registers outputs of the wait,
 // so that no consumer can be scheduled before it.
 __device__ __forceinline__ void lds_wait(short4_t& a, short4_t& b) {
@@ -246,6 +256,14 @@ __device__ __forceinline__ void lds_wait(short4_t& a, short4_t& b) {
 }
 __device__ __forceinline__ void lds_wait(short4_t& a, short4_t& b, short4_t& c, short4_t& d) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d)::"memory");
+}
+template <int N, int M>
+__device__ __forceinline__ void lds_wait_all(short4_t (&r)[N], short8_t (&s)[M]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < N; ++k) asm volatile("" : "+v"(r[k]));
+#pragma unroll
+  for (int k = 0; k < M; ++k) asm volatile("" : "+v"(s[k]));
 }
 template <int N>
 __device__ __forceinline__ void lds_wait_all(short4_t (&r)[N]) {

@@ -199,12 +199,17 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       dst[s] = v;
     }
   };
-  // keys past L read the mask of key L-1; their scores are forced to -inf anyway
+  // Raw mask values of this lane's key in each block (keys past L read key
+  // L-1).  HAS_MASK also covers rows whose length is not a multiple of 32
+  // without a user mask: the mask is then zero, and keys past L get -inf
+  // through the same extra k-step (see qk_block), so no per-score tail test
+  // is needed anywhere.
   auto load_mask = [&](uint32_t (&dst)[TL::CH / 32], int n, int kc0) {
     if constexpr (HAS_MASK) {
       const uint16_t* mrow = a.mask + ((size_t)b * N + n) * L;
 #pragma unroll
-      for (int jb = 0; jb < TL::CH / 32; ++jb) dst[jb] = mrow[min(kc0 + jb * 32 + (lane & 31), L - 1)];
+      for (int jb = 0; jb < TL::CH / 32; ++jb)
+        dst[jb] = a.mask ? mrow[min(kc0 + jb * 32 + (lane & 31), L - 1)] : 0u;
     }
   };
   // issue the asynchronous copy of tile t into LDS buffer (t & 1)
@@ -237,26 +242,32 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   floatx16 oacc[S::MB];
   float m_used = kNegInf, l_part = 0.f;
 
-  // ---- S^T block = K Q^T for 32 keys of tile buffer `buf` (mask via the extra k-step)
-  auto qk_block = [&](const uint8_t* buf, const int jb, const uint32_t mj) -> floatx16 {
-    floatx16 acc = floatx16{};
+  // ---- K operands of one 32-key block (asm reads, completed by the next PV wait)
+  auto k_fetch = [&](const uint8_t* buf, const int jb, short8_t (&kop)[S::KSTEPS_D]) {
     const int r = jb * 32 + (lane & 31);
-    short8_t kop[S::KSTEPS_D];
 #pragma unroll
     for (int s = 0; s < S::KSTEPS_D; ++s) {
       const int c = 2 * s + half;
       if (c < TL::KC) {
-        kop[s] = *reinterpret_cast<const short8_t*>(buf + (r * TL::KC + (c ^ kv_swz<TL::KC>(r))) * 16);
-      } else {  // D = 8, upper k-slots: mask augmentation (or zeros)
+        kop[s] = lds_read_b128_asm(buf, (r * TL::KC + (c ^ kv_swz<TL::KC>(r))) * 16);
+      } else {
         kop[s] = short8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        if (HAS_MASK) {
-          kop[s][0] = (short)mj;
-          kop[s][1] = (short)(a.s_lo != 0 ? mj : 0);
-        }
       }
     }
+  };
+  // ---- S^T block = K Q^T for 32 keys (mask via the extra k-step)
+  auto qk_block = [&](const short8_t (&kop_in)[S::KSTEPS_D], const uint32_t mraw, const int j0) -> floatx16 {
+    const uint32_t mj = (j0 + (lane & 31) < L) ? mraw : (uint32_t)T::kNegInfBits;
+    floatx16 acc = floatx16{};
 #pragma unroll
-    for (int s = 0; s < S::KSTEPS_D; ++s) acc = T::mfma(kop[s], qop[s], acc);
+    for (int s = 0; s < S::KSTEPS_D; ++s) {
+      short8_t kop = kop_in[s];
+      if (2 * s + half >= TL::KC && HAS_MASK) {  // D = 8, upper k-slots: mask augmentation
+        kop[0] = (short)mj;
+        kop[1] = (short)(a.s_lo != 0 ? mj : 0);
+      }
+      acc = T::mfma(kop, qop[s], acc);
+    }
     if constexpr (HAS_MASK && (D % 16) == 0) {
       short8_t ka = {0, 0, 0, 0, 0, 0, 0, 0};
       if (half == 0) {
@@ -269,9 +280,12 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   };
 
   // ---- bias, online softmax and O^T += V^T P^T for one block whose scores are in acc
-  auto softmax_pv = [&](const floatx16& acc, const uint8_t* buf, const int jb, const int j0, const u32x2 (&pb)[4]) {
+  auto softmax_pv = [&](const floatx16& acc, const uint8_t* buf, const int jb, const int j0, const u32x2 (&pb)[4],
+                        short8_t (&kpre)[S::KSTEPS_D], const int jb_pre) {
     const uint8_t* vb = buf + TL::KCH * 16;
     // V^T operands first: the reads complete under the softmax VALU work
+    // K operands two blocks ahead, completed by the wait below
+    if (jb_pre >= 0) k_fetch(buf, jb_pre, kpre);
     const int qg = lane >> 4, i16 = lane & 15, g = qg >> 1;
     short4_t vt[4 * S::MB];  // [t][mb][lo/hi]
 #pragma unroll
@@ -295,13 +309,6 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
     } else {
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) sv[rr] = acc[rr] * a.scale;
-    }
-    if (j0 + 32 > L) {
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int j = j0 + 8 * (rr / 4) + 4 * half + (rr % 4);
-        if (j >= L) sv[rr] = kNegInf;
-      }
     }
     float mb = sv[0];
 #pragma unroll
@@ -327,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       pk[rr / 2] = T::pack2(p0, p1);
       l_part = T::rowsum_add(l_part, p0, p1, pk[rr / 2]);
     }
-    lds_wait_all(vt);
+    lds_wait_all(vt, kpre);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const short8_t bop = __builtin_bit_cast(short8_t, u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]});
@@ -373,29 +380,32 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       if ((t + 1) % nchunks == 0) load_q(qnext, n1);
     }
     const uint8_t* buf = smem + (t & 1) * TL::BUF_BYTES;
-    // blocks of the tile, software-pipelined: the QK^T MFMAs of block jb+1 are
-    // issued before the softmax of block jb so that they run under its VALU work
+    // blocks of the tile, software-pipelined: while block jb is in its softmax,
+    // the QK^T MFMAs of block jb+1 run and the K operands of block jb+2 load
     const int nblk = min(TL::CH, L - kc0 + 31) / 32;
-    if constexpr (RES > 0) {
-      // the whole row is one tile: blocks unrolled so the resident bias is indexed statically
-      constexpr int NB = RES < TL::CH / 32 ? RES : TL::CH / 32;
+    {
+      constexpr int NB = (RES > 0 && RES < TL::CH / 32) ? RES : TL::CH / 32;
+      short8_t kreg[2][S::KSTEPS_D];
       floatx16 sacc[2];
-      sacc[0] = qk_block(buf, 0, mcur[0]);
+      k_fetch(buf, 0, kreg[0]);
+      if (nblk > 1) k_fetch(buf, 1, kreg[1]);
+      {
+        short4_t none[2] = {};
+        lds_wait_all(none, kreg[0]);
+        lds_wait_all(none, kreg[1]);
+      }
+      sacc[0] = qk_block(kreg[0], mcur[0], kc0);
 #pragma unroll
       for (int jb = 0; jb < NB; ++jb) {
         if (jb < nblk) {
-          if (jb + 1 < NB && jb + 1 < nblk) sacc[(jb + 1) & 1] = qk_block(buf, jb + 1, mcur[jb + 1]);
-          softmax_pv(sacc[jb & 1], buf, jb, jb * 32, pres[jb]);
-        }
-      }
-    } else {
-      floatx16 sacc[2];
-      sacc[0] = qk_block(buf, 0, mcur[0]);
-#pragma unroll
-      for (int jb = 0; jb < TL::CH / 32; ++jb) {
-        if (jb < nblk) {
-          if (jb + 1 < TL::CH / 32 && jb + 1 < nblk) sacc[(jb + 1) & 1] = qk_block(buf, jb + 1, mcur[jb + 1]);
-          softmax_pv(sacc[jb & 1], buf, jb, kc0 + jb * 32, ptile[HAS_PAIR ? jb : 0]);
+          if (jb + 1 < NB && jb + 1 < nblk)
+            sacc[(jb + 1) & 1] = qk_block(kreg[(jb + 1) & 1], mcur[jb + 1], kc0 + 32 * (jb + 1));
+          const int pre = (jb + 2 < NB && jb + 2 < nblk) ? jb + 2 : -1;
+          if constexpr (RES > 0) {
+            softmax_pv(sacc[jb & 1], buf, jb, jb * 32, pres[jb < RES ? jb : 0], kreg[jb & 1], pre);
+          } else {
+            softmax_pv(sacc[jb & 1], buf, jb, kc0 + jb * 32, ptile[HAS_PAIR ? jb : 0], kreg[jb & 1], pre);
+          }
         }
       }
     }
@@ -459,7 +469,9 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 
 template <class T, int D>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t s) {
-  const bool hm = a.mask != nullptr, hp = a.pair != nullptr;
+  // rows of a length that is not a multiple of 32 take the mask path (with a
+  // zero mask if none is given) so that keys past L are masked in the product
+  const bool hm = a.mask != nullptr || (a.L % 32) != 0, hp = a.pair != nullptr;
   if (hm && hp) return launch_fwd_t<T, D, true, true>(a, s);
   if (hm) return launch_fwd_t<T, D, true, false>(a, s);
   if (hp) return launch_fwd_t<T, D, false, true>(a, s);
