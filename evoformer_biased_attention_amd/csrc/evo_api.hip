@@ -148,20 +148,25 @@ int env_int(const char* name, int dflt) {
   return v > 0 ? v : dflt;
 }
 
-// slices per forward workgroup: enough workgroups to fill the chip, the rest
-// goes into reuse of the pair bias across n
+// slices per forward workgroup: about two workgroups per CU (512), and never
+// more than 4 slices each (measured on MI355X: larger groups lose more to the
+// tail of the grid than they gain from reusing the pair bias)
 int plan_fwd_group(const Shape& s) {
   const int64_t base = s.B * s.H * ((s.L + 127) / 128);
-  int64_t g = (s.N * base) / 1024;
+  int64_t g = (s.N * base) / 512;
   if (g < 1) g = 1;
+  if (g > 4) g = 4;
   if (g > s.N) g = s.N;
   return env_int("EVOATTN_FWD_G", (int)g);
 }
 
-// slices per bwd_q workgroup (also the dpair partial count divisor)
+// slices per bwd_q workgroup (also the dpair partial count divisor): about
+// 1024 workgroups; the kernels for rows longer than one key tile keep their
+// query tile small, so their groups stop at 8 (measured on MI355X)
 int plan_bwdq_group(const Shape& s) {
   const int64_t base = s.B * s.H * ((s.L + 31) / 32);
   int64_t g = (s.N * base) / 1024;
+  if (s.L > (s.D == 64 ? 128 : 256) && g > 8) g = 8;
   if (g < 1) g = 1;
   if (g > s.N) g = s.N;
   return env_int("EVOATTN_BWD_GQ", (int)g);
