@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libevoattn.so")
-SOURCES = ["evo_api.hip", "evo_fwd.hip", "evo_bwd.hip"]
+SOURCES = ["evo_api.hip", "evo_fwd.hip", "evo_bwd.hip", "evo_bwd_tile.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950",

@@ -395,6 +395,7 @@ evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const voi
   a.H = (int)s.H;
   a.Gq = w.gq;
   a.n_groups_q = w.ngq;
+  a.sqrt_d = (float)std::sqrt((double)s.D);
   a.scale = (float)(1.0 / std::sqrt((double)s.D));
   sqrt_split(s.D, dtype == EVO_BF16, &a.s_hi, &a.s_lo);
   hipError_t e = evo::launch_bwd(a, (int)s.D, dtype == EVO_BF16, static_cast<hipStream_t>(stream));

@@ -492,595 +492,6 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_q_kernel(BwdArgs a) {
   }
 }
 
-// ----------------------------------------------------------------- bwd_q2
-//
-// Query-stationary backward for rows that fit one key tile (L <= KVTile::CH),
-// on 16x16x32 MFMA tiles so that a wave owns 16 queries:
-//   workgroup = 4 waves = 64 queries of one (b, h) and a group of n;
-//   per n, K and V of the slice arrive in LDS by asynchronous copies
-//   (double-buffered, prefetched one slice ahead), and each wave walks all
-//   keys 32 at a time:
-//     S^T = K Q^T and dP^T = V dO^T (lane = query, 4 keys per 16-key block),
-//     P = exp(S - lse), dS^T = P (dP^T - delta),
-//     dQ^T += K^T dS^T (K^T by transposed LDS reads),
-//     dpair^T += dS^T, accumulated by an MFMA against a 0/1 selection matrix
-//     so that the n-sum costs no VALU work; it stays in registers for the
-//     whole n-group and is written once as an fp32 partial.
-constexpr int kQ2Rows = 64;
-
-template <class T, int D, bool HAS_MASK, bool HAS_PAIR, bool WANT_DPAIR>
-__global__ __launch_bounds__(256, 2) void evo_bwd_q2_kernel(BwdArgs a) {
-  using TL = KVTile<D>;
-  constexpr int KS32 = (D + 31) / 32;       // 32-wide k-steps over d
-  constexpr bool AUG_PAD = (D % 32) != 0;   // D = 8, 16: mask slots follow d in the last step
-  constexpr int KSTEPS = KS32 + ((HAS_MASK && !AUG_PAD) ? 1 : 0);
-  constexpr int NB = TL::CH / 16;           // 16-key blocks per tile
-  constexpr int MB = (D + 15) / 16;         // 16-row blocks of dQ^T
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) uint16_t smask[2][TL::CH];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, col = lane & 15;
-  const int L = a.L, H = a.H, N = a.N;
-  const int itiles = (L + kQ2Rows - 1) / kQ2Rows;
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = wg % H;
-  int rest = wg / H;
-  const int it = rest % itiles;
-  rest /= itiles;
-  const int ng = rest % a.n_groups_q;
-  const int b = rest / a.n_groups_q;
-  const int i = it * kQ2Rows + wave * 16 + col;
-  const bool i_valid = i < L;
-  const int ic = min(i, L - 1);
-  const int n_begin = ng * a.Gq, n_end = min(N, n_begin + a.Gq);
-  const int ntiles = n_end - n_begin;
-
-  // resident pair bias: block blk, lane gets pair[ic][16 blk + 4 g + 0..3]
-  u32x2 pbias[HAS_PAIR ? NB : 1];
-  if constexpr (HAS_PAIR) {
-    const uint16_t* prow = a.pair + (((size_t)b * H + h) * L + ic) * L;
-    const bool pvec = (L % 4) == 0;
-#pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-      const int j = 16 * blk + 4 * g;
-      u32x2 v;
-      if (pvec) {
-        v = *reinterpret_cast<const u32x2*>(prow + min(j, L - 4));
-      } else {
-        uint32_t t4[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) t4[u] = prow[min(j + u, L - 1)];
-        v[0] = t4[0] | (t4[1] << 16);
-        v[1] = t4[2] | (t4[3] << 16);
-      }
-      pbias[blk] = v;
-    }
-  }
-  // 0/1 selection operands: slot e of lane group g is key 4g + (e & 3) of block e / 4
-  short8_t sel[2];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    sel[0][e] = (e < 4 && 4 * g + e == col) ? T::one() : (short)0;
-    sel[1][e] = (e >= 4 && 4 * g + (e - 4) == col) ? T::one() : (short)0;
-  }
-  short8_t qaug = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (HAS_MASK && g == 0) {
-    qaug[0] = (short)a.s_hi;
-    qaug[1] = (short)a.s_lo;
-  }
-
-  short8_t qop[KS32], gop[KS32], qnx[KS32], gnx[KS32], onx[KS32];
-  float nl = 0.f, del = 0.f, nl_nx = 0.f;
-  uint32_t mreg = 0;
-  // Q, dO and O rows of this lane's query (8 columns per k-step), and its lse;
-  // delta = rowsum(dO * O) is formed from them at the start of the slice
-  auto load_rows = [&](int n) {
-    const size_t row = (((size_t)b * N + n) * L + ic) * H + h;
-#pragma unroll
-    for (int s = 0; s < KS32; ++s) {
-      const int d0 = 32 * s + 8 * g;
-      short8_t qv = {0, 0, 0, 0, 0, 0, 0, 0}, gv = {0, 0, 0, 0, 0, 0, 0, 0}, ov = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (d0 + 8 <= D) {
-        qv = *reinterpret_cast<const short8_t*>(a.q + row * D + d0);
-        gv = *reinterpret_cast<const short8_t*>(a.dout + row * D + d0);
-        ov = *reinterpret_cast<const short8_t*>(a.out + row * D + d0);
-      } else if (HAS_MASK && AUG_PAD && d0 == D) {
-        qv[0] = (short)a.s_hi;
-        qv[1] = (short)a.s_lo;
-      }
-      qnx[s] = qv;
-      gnx[s] = gv;
-      onx[s] = ov;
-    }
-    nl_nx = a.lse[(((size_t)b * N + n) * H + h) * L + ic];
-  };
-  // mask of the tile's keys; keys past L get -inf (HAS_MASK also covers
-  // ragged rows without a user mask), so the products themselves mask the tail
-  auto load_mask = [&](int n) {
-    if constexpr (HAS_MASK) {
-      if (tid < TL::CH) mreg = a.mask ? a.mask[((size_t)b * N + n) * L + min(tid, L - 1)] : 0u;
-    }
-  };
-  auto store_mask = [&](int buf) {
-    if constexpr (HAS_MASK) {
-      if (tid < TL::CH) smask[buf][tid] = (tid < L) ? (uint16_t)mreg : T::kNegInfBits;
-    }
-  };
-
-  floatx4 dpacc[WANT_DPAIR ? NB : 1];
-#pragma unroll
-  for (int blk = 0; blk < (WANT_DPAIR ? NB : 1); ++blk) dpacc[blk] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  if (ntiles > 0) {
-    load_mask(n_begin);
-    issue_kv_tile<D>(smem, a.k, a.v, ((size_t)b * N + n_begin) * L, 0, L, H, h, wave, lane);
-    load_rows(n_begin);
-    store_mask(0);
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    const int n = n_begin + t;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < KS32; ++s) {
-      qop[s] = qnx[s];
-      gop[s] = gnx[s];
-    }
-    nl = (nl_nx == kNegInf) ? kNegInf : -nl_nx * kLog2e;  // rows with no finite score: p = 0
-    {
-      // delta of this lane's query: partial dot over its columns, then the
-      // four lane groups holding the same query are summed
-      float part = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS32; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          part = __builtin_fmaf(T::to_f32((uint16_t)gnx[s][e]), T::to_f32((uint16_t)onx[s][e]), part);
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      del = part;
-      if (g == 0 && i_valid) a.delta[(((size_t)b * N + n) * H + h) * L + i] = del;
-    }
-    if (t + 1 < ntiles) {
-      load_mask(n + 1);
-      issue_kv_tile<D>(smem + ((t + 1) & 1) * TL::BUF_BYTES, a.k, a.v, ((size_t)b * N + n + 1) * L, 0, L, H, h, wave,
-                       lane);
-      load_rows(n + 1);
-    }
-    const uint8_t* kb = smem + (t & 1) * TL::BUF_BYTES;
-    const uint8_t* vb = kb + TL::KCH * 16;
-    const uint16_t* mk = smask[t & 1];
-
-    auto kop = [&](int blk, int s) -> short8_t {
-      const int r = blk * 16 + col;
-      const int c = 4 * s + g;
-      short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (c < TL::KC) {
-        op = *reinterpret_cast<const short8_t*>(kb + (r * TL::KC + (c ^ kv_swz<TL::KC>(r))) * 16);
-      } else if (HAS_MASK && AUG_PAD && c == TL::KC) {
-        const uint16_t m = mk[r];
-        op[0] = (short)m;
-        op[1] = (short)(a.s_lo != 0 ? m : 0);
-      }
-      return op;
-    };
-    auto sblk = [&](int blk) -> floatx4 {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS32; ++s) acc = T::mfma16(kop(blk, s), qop[s], acc);
-      if constexpr (HAS_MASK && !AUG_PAD) {
-        short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (g == 0) {
-          const uint16_t m = mk[blk * 16 + col];
-          op[0] = (short)m;
-          op[1] = (short)(a.s_lo != 0 ? m : 0);
-        }
-        acc = T::mfma16(op, qaug, acc);
-      }
-      return acc;
-    };
-    auto dpblk = [&](int blk) -> floatx4 {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      const int r = blk * 16 + col;
-#pragma unroll
-      for (int s = 0; s < KS32; ++s) {
-        const int c = 4 * s + g;
-        short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (c < D / 8) op = *reinterpret_cast<const short8_t*>(vb + (r * TL::VC + (c ^ kv_swz<TL::VC>(r))) * 16);
-        acc = T::mfma16(op, gop[s], acc);
-      }
-      return acc;
-    };
-
-    floatx4 dq[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) dq[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    floatx4 sc[2][2], dp[2][2];
-    sc[0][0] = sblk(0);
-    sc[0][1] = sblk(1);
-    dp[0][0] = dpblk(0);
-    dp[0][1] = dpblk(1);
-#pragma unroll
-    for (int st = 0; st < NB / 2; ++st) {
-      if (32 * st < L) {
-        const int cur = st & 1;
-        // next step's products run under this step's VALU work
-        if (st + 1 < NB / 2 && 32 * (st + 1) < L) {
-          sc[cur ^ 1][0] = sblk(2 * st + 2);
-          sc[cur ^ 1][1] = sblk(2 * st + 3);
-          dp[cur ^ 1][0] = dpblk(2 * st + 2);
-          dp[cur ^ 1][1] = dpblk(2 * st + 3);
-        }
-        // K^T operands of dQ^T for this step (transposed reads, waited on below)
-        short4_t kt[2 * MB];  // [mb][lo/hi]
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int c0 = 16 * mb + 4 * (col & 3);
-          const int r0 = 32 * st + 4 * g + (col >> 2);
-          kt[2 * mb] = lds_read_tr_asm(kb, tr_off<TL::KC>(r0, c0));
-          kt[2 * mb + 1] = lds_read_tr_asm(kb, tr_off<TL::KC>(r0 + 16, c0));
-        }
-        float ds[2][4];
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const int blk = 2 * st + hb;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float s;
-            if constexpr (HAS_PAIR) {
-              const uint32_t w = pbias[blk][r / 2];
-              s = (r & 1) ? T::fma_mix_hi(sc[cur][hb][r], a.scale, w) : T::fma_mix_lo(sc[cur][hb][r], a.scale, w);
-            } else {
-              s = sc[cur][hb][r] * a.scale;
-            }
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s, kLog2e, nl));
-            ds[hb][r] = p * (dp[cur][hb][r] - del);
-          }
-        }
-        const short8_t dsb = __builtin_bit_cast(
-            short8_t, u32x4{T::pack2(ds[0][0], ds[0][1]), T::pack2(ds[0][2], ds[0][3]), T::pack2(ds[1][0], ds[1][1]),
-                            T::pack2(ds[1][2], ds[1][3])});
-        if constexpr (WANT_DPAIR) {
-          dpacc[2 * st] = T::mfma16(sel[0], dsb, dpacc[2 * st]);
-          dpacc[2 * st + 1] = T::mfma16(sel[1], dsb, dpacc[2 * st + 1]);
-        }
-        lds_wait_all(kt);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) dq[mb] = T::mfma16(cat4(kt[2 * mb], kt[2 * mb + 1]), dsb, dq[mb]);
-      }
-    }
-    // ---- dQ = scale * dQ^T: lane holds d = 16 mb + 4 g + 0..3 of query i
-    if (i_valid) {
-      uint16_t* dqrow = a.dq + ((((size_t)b * N + n) * L + i) * H + h) * D;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int d = 16 * mb + 4 * g;
-        if (d < D) {
-          u32x2 w;
-          w[0] = T::pack2(dq[mb][0] * a.scale, dq[mb][1] * a.scale);
-          w[1] = T::pack2(dq[mb][2] * a.scale, dq[mb][3] * a.scale);
-          *reinterpret_cast<u32x2*>(dqrow + d) = w;
-        }
-      }
-    }
-    if (t + 1 < ntiles) store_mask((t + 1) & 1);
-  }
-
-  if constexpr (WANT_DPAIR) {
-    if (i_valid) {
-      float* dst = a.dpair_part + ((((size_t)ng * a.B + b) * H + h) * L + i) * L;
-#pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        const int j = 16 * blk + 4 * g;
-        if (j + 4 <= L && (L % 4) == 0) {
-          *reinterpret_cast<floatx4*>(dst + j) = dpacc[blk];
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (j + u < L) dst[j + u] = dpacc[blk][u];
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------- bwd_kv2
-//
-// Key-stationary backward for rows that fit one query tile (L <= KVTile::CH),
-// the mirror image of bwd_q2:
-//   workgroup = 4 waves = 64 keys of one (b, h) and a group of n; a wave owns
-//   16 keys, whose K and V rows sit in registers as MFMA operands;
-//   per n, Q and dO of the slice arrive in LDS by asynchronous copies (same
-//   tile layout as K/V, prefetched one slice ahead), lse and delta through
-//   LDS as well, and each wave walks all queries 32 at a time:
-//     S = Q K^T and dP = dO V^T (lane = key, 4 queries per 16-query block),
-//     P = exp(S - lse), dS = P (dP - delta),
-//     dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transposed LDS reads),
-//     dmask partial = column sums of dS, by an MFMA against a row of ones.
-//   The pair-bias columns of the workgroup's 64 keys are read once (through
-//   LDS, transposed) and stay in registers for the whole n-group.
-template <class T, int D, bool HAS_MASK, bool HAS_PAIR, bool WANT_DMASK>
-__global__ __launch_bounds__(256, 2) void evo_bwd_kv2_kernel(BwdArgs a) {
-  using TL = KVTile<D>;
-  constexpr int KS32 = (D + 31) / 32;
-  constexpr bool AUG_PAD = (D % 32) != 0;
-  constexpr int NB = TL::CH / 16;    // 16-query blocks per tile
-  constexpr int MB = (D + 15) / 16;  // 16-row blocks of dK^T, dV^T
-  constexpr int kKeys = 64;
-  constexpr int kSlab = HAS_PAIR ? TL::CH * kKeys * 2 : 0;  // pair[:, 64 keys] staged once
-  constexpr int kSmem = 2 * TL::BUF_BYTES > kSlab ? 2 * TL::BUF_BYTES : kSlab;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
-  __shared__ __attribute__((aligned(16))) float slse[2][TL::CH];  // -lse*log2e
-  __shared__ __attribute__((aligned(16))) float sdel[2][TL::CH];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, col = lane & 15;
-  const int L = a.L, H = a.H, N = a.N;
-  const int jtiles = (L + kKeys - 1) / kKeys;
-  const int ngroups = (N + a.Gq - 1) / a.Gq;
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = wg % H;
-  int rest = wg / H;
-  const int jt = rest % jtiles;
-  rest /= jtiles;
-  const int ng = rest % ngroups;
-  const int b = rest / ngroups;
-  const int j = jt * kKeys + wave * 16 + col;  // this lane's key
-  const bool j_valid = j < L;
-  const int jc = min(j, L - 1);
-  const int n_begin = ng * a.Gq, n_end = min(N, n_begin + a.Gq);
-  const int ntiles = n_end - n_begin;
-
-  // ---- pair bias, resident: block qb, lane gets pair[16 qb + 4 g + r][j], r = 0..3
-  u32x2 pbias[HAS_PAIR ? NB : 1];
-  if constexpr (HAS_PAIR) {
-    // stage pair[0..L)[64 keys] row-major (128-byte rows) with 16-byte copies,
-    // then read columns with transposed reads
-    const uint16_t* pbase = a.pair + ((size_t)b * H + h) * L * L;
-    const int kc0 = jt * kKeys;
-    for (int base = wave * 64; base < TL::CH * 8; base += 256) {
-      const int q = base + lane;
-      const int r = q >> 3, c = q & 7;
-      const int cc = min(kc0 + 8 * c, L - 8 >= 0 ? L - 8 : 0);
-      const uint16_t* src = pbase + (size_t)min(r, L - 1) * L + ((L % 8) == 0 ? cc : 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(smem + base * 16), 16, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if ((L % 8) == 0) {
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        const int row = 16 * qb + 4 * g + (col >> 2);
-        const int kcol = wave * 16 + 4 * (col & 3);
-        const short4_t v = lds_read_tr_b(smem, (row * kKeys + kcol) * 2);
-        pbias[qb] = __builtin_bit_cast(u32x2, v);
-      }
-    } else {
-      const uint16_t* prow = pbase + jc;
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        uint32_t t4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) t4[r] = prow[(size_t)min(16 * qb + 4 * g + r, L - 1) * L];
-        pbias[qb][0] = t4[0] | (t4[1] << 16);
-        pbias[qb][1] = t4[2] | (t4[3] << 16);
-      }
-    }
-    __syncthreads();
-  }
-
-  // ones in row 0 of the column-sum operand
-  short8_t ones = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (col == 0) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ones[e] = T::one();
-  }
-
-  // ---- per-slice key operands (B of S = Q K^T and dP = dO V^T): lane = key
-  short8_t kop[KS32], vop[KS32], kaug;
-  short8_t knx[KS32], vnx[KS32];
-  uint32_t mnx = 0, mcur = 0;
-  float lse_nx = 0.f, del_nx = 0.f;
-  auto load_keys = [&](int n) {
-    const size_t row = (((size_t)b * N + n) * L + jc) * H + h;
-#pragma unroll
-    for (int s = 0; s < KS32; ++s) {
-      const int d0 = 32 * s + 8 * g;
-      short8_t kv = {0, 0, 0, 0, 0, 0, 0, 0}, vv = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (d0 + 8 <= D) {
-        kv = *reinterpret_cast<const short8_t*>(a.k + row * D + d0);
-        vv = *reinterpret_cast<const short8_t*>(a.v + row * D + d0);
-      }
-      knx[s] = kv;
-      vnx[s] = vv;
-    }
-    if constexpr (HAS_MASK) mnx = a.mask ? a.mask[((size_t)b * N + n) * L + jc] : 0u;
-  };
-  auto load_rows = [&](int n) {  // lse, delta of query tid
-    if (tid < TL::CH) {
-      const size_t ri = (((size_t)b * N + n) * H + h) * L + min(tid, L - 1);
-      lse_nx = a.lse[ri];
-      del_nx = a.delta[ri];
-    }
-  };
-  auto store_rows = [&](int buf) {
-    if (tid < TL::CH) {
-      // queries past L, or with no finite score, get p = 0
-      slse[buf][tid] = (tid < L && lse_nx != kNegInf) ? -lse_nx * kLog2e : kNegInf;
-      sdel[buf][tid] = del_nx;
-    }
-  };
-
-  if (ntiles > 0) {
-    load_rows(n_begin);
-    issue_kv_tile<D>(smem, a.q, a.dout, ((size_t)b * N + n_begin) * L, 0, L, H, h, wave, lane);
-    load_keys(n_begin);
-    store_rows(0);
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    const int n = n_begin + t;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < KS32; ++s) {
-      kop[s] = knx[s];
-      vop[s] = vnx[s];
-    }
-    mcur = j_valid ? mnx : (uint32_t)T::kNegInfBits;  // keys past L: masked (not stored anyway)
-    // Q' side of the mask product is {s_hi, s_lo}; the key side {m, m'}
-    kaug = short8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    if (HAS_MASK && ((AUG_PAD && g == D / 8 - 4 * (KS32 - 1)) || (!AUG_PAD && g == 0))) {
-      kaug[0] = (short)mcur;
-      kaug[1] = (short)(a.s_lo != 0 ? mcur : 0);
-    }
-    if (AUG_PAD && HAS_MASK) {
-      // D = 8, 16: the mask slots follow d inside the last k-step
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        if (g == D / 8 - 4 * (KS32 - 1)) kop[KS32 - 1][e] = kaug[e];
-    }
-    if (t + 1 < ntiles) {
-      load_rows(n + 1);
-      issue_kv_tile<D>(smem + ((t + 1) & 1) * TL::BUF_BYTES, a.q, a.dout, ((size_t)b * N + n + 1) * L, 0, L, H, h,
-                       wave, lane);
-      load_keys(n + 1);
-    }
-    const uint8_t* qb_ = smem + (t & 1) * TL::BUF_BYTES;
-    const uint8_t* ob_ = qb_ + TL::KCH * 16;
-    const float* lrow = slse[t & 1];
-    const float* drow = sdel[t & 1];
-
-    // Q (A operand, lane = query row) with {s_hi, s_lo} in the mask slots
-    auto qrow_op = [&](int blk, int s) -> short8_t {
-      const int r = blk * 16 + col;
-      const int c = 4 * s + g;
-      short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (c < TL::KC) {
-        op = *reinterpret_cast<const short8_t*>(qb_ + (r * TL::KC + (c ^ kv_swz<TL::KC>(r))) * 16);
-      } else if (HAS_MASK && AUG_PAD && c == TL::KC) {
-        op[0] = (short)a.s_hi;
-        op[1] = (short)a.s_lo;
-      }
-      return op;
-    };
-    auto sblk = [&](int blk) -> floatx4 {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS32; ++s) acc = T::mfma16(qrow_op(blk, s), kop[s], acc);
-      if constexpr (HAS_MASK && !AUG_PAD) {
-        short8_t qa = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (g == 0) {
-          qa[0] = (short)a.s_hi;
-          qa[1] = (short)a.s_lo;
-        }
-        acc = T::mfma16(qa, kaug, acc);
-      }
-      return acc;
-    };
-    auto dpblk = [&](int blk) -> floatx4 {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      const int r = blk * 16 + col;
-#pragma unroll
-      for (int s = 0; s < KS32; ++s) {
-        const int c = 4 * s + g;
-        short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (c < D / 8) op = *reinterpret_cast<const short8_t*>(ob_ + (r * TL::VC + (c ^ kv_swz<TL::VC>(r))) * 16);
-        acc = T::mfma16(op, vop[s], acc);
-      }
-      return acc;
-    };
-
-    floatx4 dk[MB], dv[MB], dmk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      dk[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      dv[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-    floatx4 sc[2][2], dp[2][2];
-    sc[0][0] = sblk(0);
-    sc[0][1] = sblk(1);
-    dp[0][0] = dpblk(0);
-    dp[0][1] = dpblk(1);
-#pragma unroll
-    for (int st = 0; st < NB / 2; ++st) {
-      if (32 * st < L) {
-        const int cur = st & 1;
-        if (st + 1 < NB / 2 && 32 * (st + 1) < L) {
-          sc[cur ^ 1][0] = sblk(2 * st + 2);
-          sc[cur ^ 1][1] = sblk(2 * st + 3);
-          dp[cur ^ 1][0] = dpblk(2 * st + 2);
-          dp[cur ^ 1][1] = dpblk(2 * st + 3);
-        }
-        // Q^T and dO^T operands (transposed reads, waited on below)
-        short4_t tt[4 * MB];  // [mb][q lo, q hi, o lo, o hi]
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int c0 = 16 * mb + 4 * (col & 3);
-          const int r0 = 32 * st + 4 * g + (col >> 2);
-          tt[4 * mb + 0] = lds_read_tr_asm(qb_, tr_off<TL::KC>(r0, c0));
-          tt[4 * mb + 1] = lds_read_tr_asm(qb_, tr_off<TL::KC>(r0 + 16, c0));
-          tt[4 * mb + 2] = lds_read_tr_asm(ob_, tr_off<TL::VC>(r0, c0));
-          tt[4 * mb + 3] = lds_read_tr_asm(ob_, tr_off<TL::VC>(r0 + 16, c0));
-        }
-        float pv[2][4], ds[2][4];
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const int blk = 2 * st + hb;
-          const floatx4 nl4 = *reinterpret_cast<const floatx4*>(lrow + 16 * blk + 4 * g);
-          const floatx4 dl4 = *reinterpret_cast<const floatx4*>(drow + 16 * blk + 4 * g);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float s;
-            if constexpr (HAS_PAIR) {
-              const uint32_t w = pbias[blk][r / 2];
-              s = (r & 1) ? T::fma_mix_hi(sc[cur][hb][r], a.scale, w) : T::fma_mix_lo(sc[cur][hb][r], a.scale, w);
-            } else {
-              s = sc[cur][hb][r] * a.scale;
-            }
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s, kLog2e, nl4[r]));
-            pv[hb][r] = p;
-            ds[hb][r] = p * (dp[cur][hb][r] - dl4[r]);
-          }
-        }
-        const short8_t pb = __builtin_bit_cast(
-            short8_t, u32x4{T::pack2(pv[0][0], pv[0][1]), T::pack2(pv[0][2], pv[0][3]), T::pack2(pv[1][0], pv[1][1]),
-                            T::pack2(pv[1][2], pv[1][3])});
-        const short8_t db = __builtin_bit_cast(
-            short8_t, u32x4{T::pack2(ds[0][0], ds[0][1]), T::pack2(ds[0][2], ds[0][3]), T::pack2(ds[1][0], ds[1][1]),
-                            T::pack2(ds[1][2], ds[1][3])});
-        if constexpr (WANT_DMASK) dmk = T::mfma16(ones, db, dmk);
-        lds_wait_all(tt);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          dk[mb] = T::mfma16(cat4(tt[4 * mb], tt[4 * mb + 1]), db, dk[mb]);
-          dv[mb] = T::mfma16(cat4(tt[4 * mb + 2], tt[4 * mb + 3]), pb, dv[mb]);
-        }
-      }
-    }
-    // ---- dK = scale * dK^T, dV: lane holds d = 16 mb + 4 g + 0..3 of key j
-    if (j_valid) {
-      const size_t row = (((size_t)b * N + n) * L + j) * H + h;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int d = 16 * mb + 4 * g;
-        if (d < D) {
-          u32x2 wk, wv;
-          wk[0] = T::pack2(dk[mb][0] * a.scale, dk[mb][1] * a.scale);
-          wk[1] = T::pack2(dk[mb][2] * a.scale, dk[mb][3] * a.scale);
-          wv[0] = T::pack2(dv[mb][0], dv[mb][1]);
-          wv[1] = T::pack2(dv[mb][2], dv[mb][3]);
-          *reinterpret_cast<u32x2*>(a.dk + row * D + d) = wk;
-          *reinterpret_cast<u32x2*>(a.dv + row * D + d) = wv;
-        }
-      }
-      if (WANT_DMASK && g == 0) a.dmask_part[(((size_t)b * N + n) * H + h) * L + j] = dmk[0];
-    }
-    if (t + 1 < ntiles) store_rows((t + 1) & 1);
-  }
-}
-
 // ---------------------------------------------------------------- bwd_fin
 
 // Bias-gradient reductions in one launch.  Threads [0, n_pair) sum the dpair
@@ -1156,35 +567,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   const bool want_dpair = a.dpair != nullptr;
   const int nchunks = (a.L + kQChunk - 1) / kQChunk;
   const bool fits = a.L <= KVTile<D>::CH;
-  // ragged rows without a user mask take the mask path (zero mask, keys past L at -inf)
-  const bool hm_eff = HM || (a.L % 32) != 0;
   if (fits) {
-    // bwd_q2 forms delta itself and leaves it in the workspace for bwd_kv2
-    const int grid2 = a.B * a.H * ((a.L + kQ2Rows - 1) / kQ2Rows) * a.n_groups_q;
-    prof_begin(K_BWD_Q, st);
-    if (hm_eff) {
-      if (want_dpair)
-        hipLaunchKernelGGL((evo_bwd_q2_kernel<T, D, true, HP, true>), dim3(grid2), dim3(256), 0, st, a);
-      else
-        hipLaunchKernelGGL((evo_bwd_q2_kernel<T, D, true, HP, false>), dim3(grid2), dim3(256), 0, st, a);
-    } else {
-      if (want_dpair)
-        hipLaunchKernelGGL((evo_bwd_q2_kernel<T, D, false, HP, true>), dim3(grid2), dim3(256), 0, st, a);
-      else
-        hipLaunchKernelGGL((evo_bwd_q2_kernel<T, D, false, HP, false>), dim3(grid2), dim3(256), 0, st, a);
-    }
-    prof_end(K_BWD_Q, st);
-    const int gridk = a.B * a.H * ((a.L + 63) / 64) * ((a.N + a.Gq - 1) / a.Gq);
-    prof_begin(K_BWD_KV, st);
-    if (hm_eff) {
-      if (want_dmask)
-        hipLaunchKernelGGL((evo_bwd_kv2_kernel<T, D, true, HP, true>), dim3(gridk), dim3(256), 0, st, a);
-      else
-        hipLaunchKernelGGL((evo_bwd_kv2_kernel<T, D, true, HP, false>), dim3(gridk), dim3(256), 0, st, a);
-    } else {
-      hipLaunchKernelGGL((evo_bwd_kv2_kernel<T, D, false, HP, false>), dim3(gridk), dim3(256), 0, st, a);
-    }
-    prof_end(K_BWD_KV, st);
+    const hipError_t e = launch_bwd_tile(a, D, std::is_same<T, BF16>::value, st);
+    if (e != hipSuccess) return e;
   } else {
     {
       const int64_t rows = (int64_t)a.B * a.N * a.L * a.H;

@@ -1,0 +1,664 @@
+// Backward of Evoformer biased attention for rows that fit one key tile
+// (L <= 256, or L <= 128 at D = 64), gfx950.
+//
+// DeepSpeed4Science guide §3.7: recompute P from the saved fp32 lse, derive
+// delta = rowsum(dO * O), then dQ, dK, dV and the two bias gradients, the bias
+// gradients accumulated in fp32:
+//   P = exp(S - lse),  dS = P (dP - delta),  dP = dO V^T
+//   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO
+//   dmask[b,n,j] = sum_h sum_i dS,  dpair[b,h,i,j] = sum_n dS
+//
+// Two kernels, each recomputing S and P (the reductions run along different
+// axes and stay on chip without atomics):
+//   bwd_q3   64 queries of one (b, h) and a group of n per workgroup: dQ,
+//            delta (written for bwd_kv3), and dpair summed over the n-group in
+//            registers, written once per group as an fp32 partial;
+//   bwd_kv3  64 keys of one (b, h) and a group of n per workgroup: dK, dV and
+//            the per-head dmask partials.
+// Both use v_mfma_f32_16x16x32 tiles (a wave owns 16 rows) and take as much
+// per-score work off the vector ALU as the accumulator layout allows:
+//   - the mask enters the score MFMA as its accumulator input (sqrt(D) * mask,
+//     -inf for keys past L), so it costs neither a VALU op nor an MFMA;
+//   - -delta enters the dP MFMA the same way, so dS = P * acc is one multiply;
+//   - the n-sum of dpair is an MFMA against an identity operand;
+//   - LDS operand reads use the instruction's immediate offset field.
+// Per score the vector ALU then does: the bias add (fused with the scale),
+// the exp argument, the exp, dS = P * acc and a share of the 16-bit packing.
+#include "evo_common.h"
+#include "evo_kernels.h"
+#include "evo_prof.h"
+
+namespace evo {
+
+constexpr int kTileRows = 64;  // queries (bwd_q3) or keys (bwd_kv3) per workgroup
+
+// Per-thread byte offsets, relative to the first element of a (b, n) slice,
+// of the 16-byte chunks this thread copies into a tile (rows = keys [0, CH),
+// clamped to L - 1; K-layout chunks first, then V-layout chunks).  They do not
+// depend on n, so the per-slice copy is a base pointer plus these offsets.
+template <int D>
+__device__ __forceinline__ void tile_chunk_offsets(uint32_t (&off)[KVTile<D>::TCH / 256], int L, int H, int h, int wave,
+                                                   int lane) {
+  using TL = KVTile<D>;
+#pragma unroll
+  for (int c = 0; c < TL::TCH / 256; ++c) {
+    const int q = wave * 64 + 256 * c + lane;
+    int r, cc;
+    if (q < TL::KCH) {
+      r = q / TL::KC;
+      cc = (q % TL::KC) ^ kv_swz<TL::KC>(r);
+    } else {
+      const int q2 = q - TL::KCH;
+      r = q2 / TL::VC;
+      cc = (q2 % TL::VC) ^ kv_swz<TL::VC>(r);
+      if (cc >= D / 8) cc = 0;  // columns the transposed reads touch but never use
+    }
+    const int j = min(r, L - 1);
+    off[c] = (uint32_t)((((size_t)j * H + h) * D + 8 * cc) * 2);
+  }
+}
+
+// Issue the asynchronous copies of one slice's tile (rows of `kx` in the K
+// layout, rows of `vx` in the V layout) into an LDS buffer.
+template <int D>
+__device__ __forceinline__ void issue_tile(uint8_t* buf, const uint16_t* kx, const uint16_t* vx,
+                                           const uint32_t (&off)[KVTile<D>::TCH / 256], int wave) {
+  using TL = KVTile<D>;
+#pragma unroll
+  for (int c = 0; c < TL::TCH / 256; ++c) {
+    const int base = wave * 64 + 256 * c;
+    const char* src = reinterpret_cast<const char*>(base < TL::KCH ? kx : vx) + off[c];
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(buf + base * 16), 16, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------- bwd_q3
+//
+// Wave w owns queries 16w..16w+15 of the tile (lane = query, S^T layout).
+// Per n the K and V rows of the slice arrive in LDS (double-buffered,
+// prefetched one slice ahead); per 32-key step:
+//   S^T  = K Q^T + sqrt(D) mask          (mask as accumulator input)
+//   dP^T = V dO^T - delta                (-delta as accumulator input)
+//   P = exp2((S*scale + pair) log2e - lse log2e),  dS^T = P dP^T
+//   dQ^T += K^T dS^T                     (K^T by transposed LDS reads)
+//   dpair^T[block] += I dS^T[block]      (16x16x16 MFMA against an identity)
+template <class T, int D, bool HAS_PAIR, bool WANT_DPAIR>
+__global__ __launch_bounds__(256, 2) void evo_bwd_q3_kernel(BwdArgs a) {
+  using TL = KVTile<D>;
+  constexpr int KS32 = (D + 31) / 32;  // 32-wide k-steps over d
+  constexpr int NB = TL::CH / 16;      // 16-key blocks per tile
+  constexpr int NSTEP = TL::CH / 32;   // 32-key steps per tile
+  constexpr int MB = (D + 15) / 16;    // 16-row blocks of dQ^T
+  constexpr int KC = TL::KC, VC = TL::VC;
+  constexpr int NCH = TL::TCH / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) float smk[2][TL::CH];  // sqrt(D) * mask of key j, -inf past L
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int L = a.L, H = a.H, N = a.N;
+  const int itiles = (L + kTileRows - 1) / kTileRows;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = wg % H;
+  int rest = wg / H;
+  const int it = rest % itiles;
+  rest /= itiles;
+  const int ng = rest % a.n_groups_q;
+  const int b = rest / a.n_groups_q;
+  const int i = it * kTileRows + wave * 16 + col;
+  const bool i_valid = i < L;
+  const int ic = min(i, L - 1);
+  const int n_begin = ng * a.Gq, n_end = min(N, n_begin + a.Gq);
+  const int ntiles = n_end - n_begin;
+  const float scale = a.scale, c1 = a.scale * kLog2e;
+
+  // resident pair bias: block blk, lane gets pair[ic][16 blk + 4 g + 0..3]
+  u32x2 pbias[HAS_PAIR ? NB : 1];
+  if constexpr (HAS_PAIR) {
+    const uint16_t* prow = a.pair + (((size_t)b * H + h) * L + ic) * L;
+    const bool pvec = (L % 4) == 0;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const int j = 16 * blk + 4 * g;
+      u32x2 v;
+      if (pvec) {
+        v = *reinterpret_cast<const u32x2*>(prow + min(j, L - 4));
+      } else {
+        uint32_t t4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) t4[u] = prow[min(j + u, L - 1)];
+        v[0] = t4[0] | (t4[1] << 16);
+        v[1] = t4[2] | (t4[3] << 16);
+      }
+      pbias[blk] = v;
+    }
+  }
+  // identity A operand of the 16x16x16 dpair MFMA: lane (row col, group g) holds A[col][4g + e]
+  short4_t ident;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ident[e] = (4 * g + e == col) ? T::one() : (short)0;
+
+  uint32_t coff[NCH];
+  tile_chunk_offsets<D>(coff, L, H, h, wave, lane);
+
+  short8_t qop[KS32], gop[KS32], qnx[KS32], gnx[KS32], onx[KS32];
+  float lse_nx = 0.f;
+  uint32_t mraw = 0;
+  const bool mask_thread = tid < TL::CH;
+  auto load_rows = [&](int n) {
+    const size_t row = (((size_t)b * N + n) * L + ic) * H + h;
+#pragma unroll
+    for (int s = 0; s < KS32; ++s) {
+      const int d0 = 32 * s + 8 * g;
+      short8_t qv = {0, 0, 0, 0, 0, 0, 0, 0}, gv = qv, ov = qv;
+      if (d0 + 8 <= D) {
+        qv = *reinterpret_cast<const short8_t*>(a.q + row * D + d0);
+        gv = *reinterpret_cast<const short8_t*>(a.dout + row * D + d0);
+        ov = *reinterpret_cast<const short8_t*>(a.out + row * D + d0);
+      }
+      qnx[s] = qv;
+      gnx[s] = gv;
+      onx[s] = ov;
+    }
+    lse_nx = a.lse[(((size_t)b * N + n) * H + h) * L + ic];
+    if (mask_thread) mraw = a.mask ? a.mask[((size_t)b * N + n) * L + min(tid, L - 1)] : 0u;
+  };
+  auto store_mask = [&](int buf) {
+    if (mask_thread) smk[buf][tid] = (tid < L) ? T::to_f32((uint16_t)mraw) * a.sqrt_d : kNegInf;
+  };
+  auto slice_ptr = [&](const uint16_t* base, int n) { return base + ((size_t)b * N + n) * L * H * D; };
+
+  floatx4 dpacc[WANT_DPAIR ? NB : 1];
+#pragma unroll
+  for (int blk = 0; blk < (WANT_DPAIR ? NB : 1); ++blk) dpacc[blk] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (ntiles > 0) {
+    load_rows(n_begin);
+    issue_tile<D>(smem, slice_ptr(a.k, n_begin), slice_ptr(a.v, n_begin), coff, wave);
+    store_mask(0);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    const int n = n_begin + t;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < KS32; ++s) {
+      qop[s] = qnx[s];
+      gop[s] = gnx[s];
+    }
+    const float nl = (lse_nx == kNegInf) ? kNegInf : -lse_nx * kLog2e;  // rows with no finite score: P = 0
+    float del;
+    {
+      // delta of this lane's query: dot over its 8 columns, then over the four
+      // lane groups that hold the same query
+      float part = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS32; ++s) {
+        const u32x4 gw = __builtin_bit_cast(u32x4, gnx[s]), ow = __builtin_bit_cast(u32x4, onx[s]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part = T::dot2(gw[e], ow[e], part);
+      }
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      del = part;
+      if (g == 0 && i_valid) a.delta[(((size_t)b * N + n) * H + h) * L + i] = del;
+    }
+    const floatx4 ndel = {-del, -del, -del, -del};
+    if (t + 1 < ntiles) {
+      issue_tile<D>(smem + ((t + 1) & 1) * TL::BUF_BYTES, slice_ptr(a.k, n + 1), slice_ptr(a.v, n + 1), coff, wave);
+      load_rows(n + 1);
+    }
+    const uint8_t* kb = smem + (t & 1) * TL::BUF_BYTES;
+    const uint8_t* vb = kb + TL::KCH * 16;
+    const float* mkb = &smk[t & 1][4 * g];
+    // row (key) 16 blk + col of a tile: the swizzle depends on col only, so a
+    // block's operands sit at a fixed offset from the lane's base
+    const uint8_t* kbase[KS32];
+    const uint8_t* vbase[KS32];
+#pragma unroll
+    for (int s = 0; s < KS32; ++s) {
+      const int c = 4 * s + g;
+      kbase[s] = kb + (col * KC + ((c < KC ? c : 0) ^ kv_swz<KC>(col))) * 16;
+      vbase[s] = vb + (col * VC + ((c < VC ? c : 0) ^ kv_swz<VC>(col))) * 16;
+    }
+    // transposed K^T reads: row 4g + col/4 (+32 per step, +16 for the upper
+    // half), column 16 mb + 4 (col % 4); the swizzle again depends on the lane only
+    uint32_t ktaddr[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      ktaddr[mb] = lds_addr(kb) + tr_off<KC>(4 * g + (col >> 2), 16 * mb + 4 * (col & 3));
+
+    auto sblk = [&](int blk) -> floatx4 {
+      floatx4 acc = *reinterpret_cast<const floatx4*>(mkb + 16 * blk);
+#pragma unroll
+      for (int s = 0; s < KS32; ++s) {
+        short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (4 * s + g < KC) op = *reinterpret_cast<const short8_t*>(kbase[s] + blk * 16 * KC * 16);
+        acc = T::mfma16(op, qop[s], acc);
+      }
+      return acc;
+    };
+    auto dpblk = [&](int blk) -> floatx4 {
+      floatx4 acc = ndel;
+#pragma unroll
+      for (int s = 0; s < KS32; ++s) {
+        short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (4 * s + g < D / 8) op = *reinterpret_cast<const short8_t*>(vbase[s] + blk * 16 * VC * 16);
+        acc = T::mfma16(op, gop[s], acc);
+      }
+      return acc;
+    };
+
+    floatx4 dq[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) dq[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 sc[2][2], dp[2][2];
+    sc[0][0] = sblk(0);
+    sc[0][1] = sblk(1);
+    dp[0][0] = dpblk(0);
+    dp[0][1] = dpblk(1);
+    static_for<0, NSTEP>([&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      constexpr int cur = st & 1;
+      // the next step's products are issued before this step's vector work
+      // (rows past L read finite tile data and are never used)
+      if constexpr (st + 1 < NSTEP) {
+        sc[cur ^ 1][0] = sblk(2 * st + 2);
+        sc[cur ^ 1][1] = sblk(2 * st + 3);
+        dp[cur ^ 1][0] = dpblk(2 * st + 2);
+        dp[cur ^ 1][1] = dpblk(2 * st + 3);
+      }
+      if (32 * st < L) {
+        short4_t kt[2 * MB];  // [mb][lo/hi 16 keys]
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          kt[2 * mb] = lds_tr_imm<st * 32 * KC * 16>(ktaddr[mb]);
+          kt[2 * mb + 1] = lds_tr_imm<st * 32 * KC * 16 + 16 * KC * 16>(ktaddr[mb]);
+        }
+        float ds[2][4];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int blk = 2 * st + hb;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x;
+            if constexpr (HAS_PAIR) {
+              const uint32_t w = pbias[blk][r / 2];
+              const float sv = (r & 1) ? T::fma_mix_hi(sc[cur][hb][r], scale, w) : T::fma_mix_lo(sc[cur][hb][r], scale, w);
+              x = __builtin_fmaf(sv, kLog2e, nl);
+            } else {
+              x = __builtin_fmaf(sc[cur][hb][r], c1, nl);
+            }
+            ds[hb][r] = __builtin_amdgcn_exp2f(x) * dp[cur][hb][r];
+          }
+        }
+        const u32x4 dw = {T::pack2(ds[0][0], ds[0][1]), T::pack2(ds[0][2], ds[0][3]), T::pack2(ds[1][0], ds[1][1]),
+                          T::pack2(ds[1][2], ds[1][3])};
+        const short8_t dsb = __builtin_bit_cast(short8_t, dw);
+        if constexpr (WANT_DPAIR) {
+          dpacc[2 * st] = T::mfma16k16(ident, __builtin_bit_cast(short4_t, u32x2{dw[0], dw[1]}), dpacc[2 * st]);
+          dpacc[2 * st + 1] = T::mfma16k16(ident, __builtin_bit_cast(short4_t, u32x2{dw[2], dw[3]}), dpacc[2 * st + 1]);
+        }
+        lds_wait_all(kt);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) dq[mb] = T::mfma16(cat4(kt[2 * mb], kt[2 * mb + 1]), dsb, dq[mb]);
+      }
+    });
+    // ---- dQ = scale * dQ^T: lane holds d = 16 mb + 4 g + 0..3 of query i
+    if (i_valid) {
+      uint16_t* dqrow = a.dq + ((((size_t)b * N + n) * L + i) * H + h) * D;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int d = 16 * mb + 4 * g;
+        if (d < D) {
+          u32x2 w;
+          w[0] = T::pack2(dq[mb][0] * scale, dq[mb][1] * scale);
+          w[1] = T::pack2(dq[mb][2] * scale, dq[mb][3] * scale);
+          *reinterpret_cast<u32x2*>(dqrow + d) = w;
+        }
+      }
+    }
+    if (t + 1 < ntiles) store_mask((t + 1) & 1);
+  }
+
+  if constexpr (WANT_DPAIR) {
+    if (i_valid) {
+      float* dst = a.dpair_part + ((((size_t)ng * a.B + b) * H + h) * L + i) * L;
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        const int j = 16 * blk + 4 * g;
+        if (j + 4 <= L && (L % 4) == 0) {
+          *reinterpret_cast<floatx4*>(dst + j) = dpacc[blk];
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (j + u < L) dst[j + u] = dpacc[blk][u];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bwd_kv3
+//
+// The mirror image: wave w owns keys 16w..16w+15 of the workgroup's 64 (lane
+// = key, S layout with query rows); K and V rows of the lane's key are the
+// MFMA B operands; per n the Q and dO rows of the slice arrive in LDS
+// (same tile layout), -lse log2e and -delta per query through LDS.  Per
+// 32-query step:
+//   S  = Q K^T + sqrt(D) mask_j          (lane constant as accumulator input)
+//   dP = dO V^T - delta_i                (accumulator input read from LDS)
+//   P = exp2(...),  dS = P dP
+//   dV^T += dO^T P,  dK^T += Q^T dS      (dO^T, Q^T by transposed LDS reads)
+//   dmask partial += column sums of dS   (MFMA against a row of ones)
+// The pair-bias columns of the 64 keys are read once per workgroup (through
+// LDS, transposed) and stay in registers for the whole n-group.
+template <class T, int D, bool HAS_PAIR, bool WANT_DMASK>
+__global__ __launch_bounds__(256, 2) void evo_bwd_kv3_kernel(BwdArgs a) {
+  using TL = KVTile<D>;
+  constexpr int KS32 = (D + 31) / 32;
+  constexpr int NB = TL::CH / 16;  // 16-query blocks per tile
+  constexpr int NSTEP = TL::CH / 32;
+  constexpr int MB = (D + 15) / 16;
+  constexpr int KC = TL::KC, VC = TL::VC;
+  constexpr int NCH = TL::TCH / 256;
+  constexpr int kSlab = HAS_PAIR ? TL::CH * kTileRows * 2 : 0;  // pair[:, 64 keys] staged once
+  constexpr int kSmem = 2 * TL::BUF_BYTES > kSlab ? 2 * TL::BUF_BYTES : kSlab;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+  __shared__ __attribute__((aligned(16))) float slse[2][TL::CH];  // -lse log2e; -inf past L / no finite score
+  __shared__ __attribute__((aligned(16))) float sndel[2][TL::CH]; // -delta
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int L = a.L, H = a.H, N = a.N;
+  const int jtiles = (L + kTileRows - 1) / kTileRows;
+  const int ngroups = (N + a.Gq - 1) / a.Gq;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = wg % H;
+  int rest = wg / H;
+  const int jt = rest % jtiles;
+  rest /= jtiles;
+  const int ng = rest % ngroups;
+  const int b = rest / ngroups;
+  const int j = jt * kTileRows + wave * 16 + col;  // this lane's key
+  const bool j_valid = j < L;
+  const int jc = min(j, L - 1);
+  const int n_begin = ng * a.Gq, n_end = min(N, n_begin + a.Gq);
+  const int ntiles = n_end - n_begin;
+  const float scale = a.scale, c1 = a.scale * kLog2e;
+
+  // ---- pair bias, resident: block qb, lane gets pair[16 qb + 4 g + r][j], r = 0..3
+  u32x2 pbias[HAS_PAIR ? NB : 1];
+  if constexpr (HAS_PAIR) {
+    const uint16_t* pbase = a.pair + ((size_t)b * H + h) * L * L;
+    if ((L % 8) == 0) {
+      // stage pair[0..L)[64 keys] row-major (128-byte rows) with 16-byte
+      // copies, then read columns with transposed reads
+      const int kc0 = jt * kTileRows;
+      for (int base = wave * 64; base < TL::CH * 8; base += 256) {
+        const int q = base + lane;
+        const int r = q >> 3, c = q & 7;
+        const uint16_t* src = pbase + (size_t)min(r, L - 1) * L + min(kc0 + 8 * c, L - 8);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(smem + base * 16), 16, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) {
+        const int row = 16 * qb + 4 * g + (col >> 2);
+        const int kcol = wave * 16 + 4 * (col & 3);
+        const short4_t v = lds_read_tr_b(smem, (row * kTileRows + kcol) * 2);
+        pbias[qb] = __builtin_bit_cast(u32x2, v);
+      }
+      __syncthreads();
+    } else {
+      const uint16_t* prow = pbase + jc;
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) {
+        uint32_t t4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t4[r] = prow[(size_t)min(16 * qb + 4 * g + r, L - 1) * L];
+        pbias[qb][0] = t4[0] | (t4[1] << 16);
+        pbias[qb][1] = t4[2] | (t4[3] << 16);
+      }
+    }
+  }
+
+  // ones in row 0 of the column-sum operand
+  short8_t ones = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (col == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = T::one();
+  }
+
+  uint32_t coff[NCH];
+  tile_chunk_offsets<D>(coff, L, H, h, wave, lane);
+
+  // ---- per-slice key operands (B of S = Q K^T and dP = dO V^T): lane = key
+  short8_t kop[KS32], vop[KS32], knx[KS32], vnx[KS32];
+  uint32_t mnx = 0;
+  float lse_nx = 0.f, del_nx = 0.f;
+  const bool row_thread = tid < TL::CH;
+  auto load_keys = [&](int n) {
+    const size_t row = (((size_t)b * N + n) * L + jc) * H + h;
+#pragma unroll
+    for (int s = 0; s < KS32; ++s) {
+      const int d0 = 32 * s + 8 * g;
+      short8_t kv = {0, 0, 0, 0, 0, 0, 0, 0}, vv = kv;
+      if (d0 + 8 <= D) {
+        kv = *reinterpret_cast<const short8_t*>(a.k + row * D + d0);
+        vv = *reinterpret_cast<const short8_t*>(a.v + row * D + d0);
+      }
+      knx[s] = kv;
+      vnx[s] = vv;
+    }
+    mnx = a.mask ? a.mask[((size_t)b * N + n) * L + jc] : 0u;
+    if (row_thread) {
+      const size_t ri = (((size_t)b * N + n) * H + h) * L + min(tid, L - 1);
+      lse_nx = a.lse[ri];
+      del_nx = a.delta[ri];
+    }
+  };
+  auto store_rows = [&](int buf) {
+    if (row_thread) {
+      // queries past L, or with no finite score, get P = 0
+      slse[buf][tid] = (tid < L && lse_nx != kNegInf) ? -lse_nx * kLog2e : kNegInf;
+      sndel[buf][tid] = -del_nx;
+    }
+  };
+  auto slice_ptr = [&](const uint16_t* base, int n) { return base + ((size_t)b * N + n) * L * H * D; };
+
+  if (ntiles > 0) {
+    load_keys(n_begin);
+    issue_tile<D>(smem, slice_ptr(a.q, n_begin), slice_ptr(a.dout, n_begin), coff, wave);
+    store_rows(0);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    const int n = n_begin + t;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < KS32; ++s) {
+      kop[s] = knx[s];
+      vop[s] = vnx[s];
+    }
+    // sqrt(D) * mask of the lane's key as the score accumulator input
+    const float mk = j_valid ? T::to_f32((uint16_t)mnx) * a.sqrt_d : kNegInf;
+    const floatx4 mk4 = {mk, mk, mk, mk};
+    if (t + 1 < ntiles) {
+      issue_tile<D>(smem + ((t + 1) & 1) * TL::BUF_BYTES, slice_ptr(a.q, n + 1), slice_ptr(a.dout, n + 1), coff, wave);
+      load_keys(n + 1);
+    }
+    const uint8_t* qb_ = smem + (t & 1) * TL::BUF_BYTES;
+    const uint8_t* ob_ = qb_ + TL::KCH * 16;
+    const float* lrow = &slse[t & 1][4 * g];
+    const float* drow = &sndel[t & 1][4 * g];
+    const uint8_t* qbase[KS32];
+    const uint8_t* obase[KS32];
+#pragma unroll
+    for (int s = 0; s < KS32; ++s) {
+      const int c = 4 * s + g;
+      qbase[s] = qb_ + (col * KC + ((c < KC ? c : 0) ^ kv_swz<KC>(col))) * 16;
+      obase[s] = ob_ + (col * VC + ((c < VC ? c : 0) ^ kv_swz<VC>(col))) * 16;
+    }
+    uint32_t qtaddr[MB], otaddr[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      qtaddr[mb] = lds_addr(qb_) + tr_off<KC>(4 * g + (col >> 2), 16 * mb + 4 * (col & 3));
+      otaddr[mb] = lds_addr(ob_) + tr_off<VC>(4 * g + (col >> 2), 16 * mb + 4 * (col & 3));
+    }
+
+    auto sblk = [&](int blk) -> floatx4 {
+      floatx4 acc = mk4;
+#pragma unroll
+      for (int s = 0; s < KS32; ++s) {
+        short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (4 * s + g < KC) op = *reinterpret_cast<const short8_t*>(qbase[s] + blk * 16 * KC * 16);
+        acc = T::mfma16(op, kop[s], acc);
+      }
+      return acc;
+    };
+    auto dpblk = [&](int blk) -> floatx4 {
+      floatx4 acc = *reinterpret_cast<const floatx4*>(drow + 16 * blk);
+#pragma unroll
+      for (int s = 0; s < KS32; ++s) {
+        short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (4 * s + g < D / 8) op = *reinterpret_cast<const short8_t*>(obase[s] + blk * 16 * VC * 16);
+        acc = T::mfma16(op, vop[s], acc);
+      }
+      return acc;
+    };
+
+    floatx4 dk[MB], dv[MB], dmk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      dk[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      dv[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    floatx4 sc[2][2], dp[2][2];
+    sc[0][0] = sblk(0);
+    sc[0][1] = sblk(1);
+    dp[0][0] = dpblk(0);
+    dp[0][1] = dpblk(1);
+    static_for<0, NSTEP>([&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      constexpr int cur = st & 1;
+      if constexpr (st + 1 < NSTEP) {
+        sc[cur ^ 1][0] = sblk(2 * st + 2);
+        sc[cur ^ 1][1] = sblk(2 * st + 3);
+        dp[cur ^ 1][0] = dpblk(2 * st + 2);
+        dp[cur ^ 1][1] = dpblk(2 * st + 3);
+      }
+      if (32 * st < L) {
+        short4_t tt[4 * MB];  // [mb][q lo, q hi, o lo, o hi]
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          tt[4 * mb + 0] = lds_tr_imm<st * 32 * KC * 16>(qtaddr[mb]);
+          tt[4 * mb + 1] = lds_tr_imm<st * 32 * KC * 16 + 16 * KC * 16>(qtaddr[mb]);
+          tt[4 * mb + 2] = lds_tr_imm<st * 32 * VC * 16>(otaddr[mb]);
+          tt[4 * mb + 3] = lds_tr_imm<st * 32 * VC * 16 + 16 * VC * 16>(otaddr[mb]);
+        }
+        float pv[2][4], ds[2][4];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int blk = 2 * st + hb;
+          const floatx4 nl4 = *reinterpret_cast<const floatx4*>(lrow + 16 * blk);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x;
+            if constexpr (HAS_PAIR) {
+              const uint32_t w = pbias[blk][r / 2];
+              const float sv = (r & 1) ? T::fma_mix_hi(sc[cur][hb][r], scale, w) : T::fma_mix_lo(sc[cur][hb][r], scale, w);
+              x = __builtin_fmaf(sv, kLog2e, nl4[r]);
+            } else {
+              x = __builtin_fmaf(sc[cur][hb][r], c1, nl4[r]);
+            }
+            const float p = __builtin_amdgcn_exp2f(x);
+            pv[hb][r] = p;
+            ds[hb][r] = p * dp[cur][hb][r];
+          }
+        }
+        const short8_t pb = __builtin_bit_cast(
+            short8_t, u32x4{T::pack2(pv[0][0], pv[0][1]), T::pack2(pv[0][2], pv[0][3]), T::pack2(pv[1][0], pv[1][1]),
+                            T::pack2(pv[1][2], pv[1][3])});
+        const short8_t db = __builtin_bit_cast(
+            short8_t, u32x4{T::pack2(ds[0][0], ds[0][1]), T::pack2(ds[0][2], ds[0][3]), T::pack2(ds[1][0], ds[1][1]),
+                            T::pack2(ds[1][2], ds[1][3])});
+        if constexpr (WANT_DMASK) dmk = T::mfma16(ones, db, dmk);
+        lds_wait_all(tt);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          dk[mb] = T::mfma16(cat4(tt[4 * mb], tt[4 * mb + 1]), db, dk[mb]);
+          dv[mb] = T::mfma16(cat4(tt[4 * mb + 2], tt[4 * mb + 3]), pb, dv[mb]);
+        }
+      }
+    });
+    // ---- dK = scale * dK^T, dV: lane holds d = 16 mb + 4 g + 0..3 of key j
+    if (j_valid) {
+      const size_t row = (((size_t)b * N + n) * L + j) * H + h;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int d = 16 * mb + 4 * g;
+        if (d < D) {
+          u32x2 wk, wv;
+          wk[0] = T::pack2(dk[mb][0] * scale, dk[mb][1] * scale);
+          wk[1] = T::pack2(dk[mb][2] * scale, dk[mb][3] * scale);
+          wv[0] = T::pack2(dv[mb][0], dv[mb][1]);
+          wv[1] = T::pack2(dv[mb][2], dv[mb][3]);
+          *reinterpret_cast<u32x2*>(a.dk + row * D + d) = wk;
+          *reinterpret_cast<u32x2*>(a.dv + row * D + d) = wv;
+        }
+      }
+      if (WANT_DMASK && g == 0) a.dmask_part[(((size_t)b * N + n) * H + h) * L + j] = dmk[0];
+    }
+    if (t + 1 < ntiles) store_rows((t + 1) & 1);
+  }
+}
+
+// ------------------------------------------------------------------ launch
+
+template <class T, int D, bool HP>
+static hipError_t launch_tile_t(const BwdArgs& a, hipStream_t st) {
+  const bool want_dmask = a.dmask != nullptr;
+  const bool want_dpair = a.dpair != nullptr;
+  // bwd_q3 forms delta and leaves it in the workspace for bwd_kv3
+  const int gridq = a.B * a.H * ((a.L + kTileRows - 1) / kTileRows) * a.n_groups_q;
+  prof_begin(K_BWD_Q, st);
+  if (want_dpair)
+    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, true>), dim3(gridq), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, false>), dim3(gridq), dim3(256), 0, st, a);
+  prof_end(K_BWD_Q, st);
+  const int gridk = a.B * a.H * ((a.L + kTileRows - 1) / kTileRows) * ((a.N + a.Gq - 1) / a.Gq);
+  prof_begin(K_BWD_KV, st);
+  if (want_dmask)
+    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, true>), dim3(gridk), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, false>), dim3(gridk), dim3(256), 0, st, a);
+  prof_end(K_BWD_KV, st);
+  return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t launch_tile_d(const BwdArgs& a, hipStream_t st) {
+  return a.pair ? launch_tile_t<T, D, true>(a, st) : launch_tile_t<T, D, false>(a, st);
+}
+
+template <class T>
+static hipError_t launch_tile_dt(const BwdArgs& a, int D, hipStream_t st) {
+  switch (D) {
+    case 8: return launch_tile_d<T, 8>(a, st);
+    case 16: return launch_tile_d<T, 16>(a, st);
+    case 32: return launch_tile_d<T, 32>(a, st);
+    case 64: return launch_tile_d<T, 64>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_tile(const BwdArgs& a, int D, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_tile_dt<BF16>(a, D, stream) : launch_tile_dt<F16>(a, D, stream);
+}
+
+}  // namespace evo

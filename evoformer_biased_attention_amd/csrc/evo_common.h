@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace evo {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -58,6 +60,16 @@ struct F16 {
   }
   static __device__ __forceinline__ floatx4 mfma16(const short8_t& a, const short8_t& b, const floatx4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+  }
+  // v_mfma_f32_16x16x16_f16 (same issue cost as 16x16x32 on gfx950, half the k)
+  static __device__ __forceinline__ floatx4 mfma16k16(const short4_t& a, const short4_t& b, const floatx4& c) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, a), __builtin_bit_cast(h4, b), c, 0, 0, 0);
+  }
+  // c + a.lo*b.lo + a.hi*b.hi for packed pairs, fp32 accumulation
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
   }
   static __device__ __forceinline__ short one() { return (short)0x3c00; }
   static constexpr uint16_t kNegInfBits = 0xfc00;
@@ -103,6 +115,14 @@ struct BF16 {
   }
   static __device__ __forceinline__ floatx4 mfma16(const short8_t& a, const short8_t& b, const floatx4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ floatx4 mfma16k16(const short4_t& a, const short4_t& b, const floatx4& c) {
+    typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(b4, a), __builtin_bit_cast(b4, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), c, false);
   }
   static __device__ __forceinline__ short one() { return (short)0x3f80; }
   static constexpr uint16_t kNegInfBits = 0xff80;
@@ -287,6 +307,30 @@ __host__ __device__ constexpr int padded_stride_elems(int min_elems) {
   int q = (dw + 3) / 4;                 // quads of dwords
   if ((q & 1) == 0) q += 1;             // odd number of quads
   return q * 8;                         // back to 16-bit elements
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(static_cast<F&&>(f));
+  }
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Transposed read (as lds_read_tr_asm) at a compile-time byte offset from a
+// base address register: the offset goes into the instruction's 16-bit field.
+template <int OFF>
+__device__ __forceinline__ short4_t lds_tr_imm(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return __builtin_bit_cast(short4_t, r);
 }
 
 }  // namespace evo

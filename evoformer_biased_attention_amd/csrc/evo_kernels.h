@@ -45,6 +45,7 @@ struct BwdArgs {
   int Gq;          // slices per bwd_q workgroup
   int n_groups_q;
   float scale;
+  float sqrt_d;    // sqrt(D) in fp32 (the masks enter the score accumulators pre-multiplied by it)
   uint16_t s_hi, s_lo;
 };
 
@@ -63,5 +64,7 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 
 hipError_t launch_fwd(FwdArgs a, int D, bool bf16, hipStream_t stream);
 hipError_t launch_bwd(BwdArgs a, int D, bool bf16, hipStream_t stream);
+// backward for rows that fit one key tile (L <= 256, or 128 at D = 64): bwd_q3 then bwd_kv3
+hipError_t launch_bwd_tile(const BwdArgs& a, int D, bool bf16, hipStream_t stream);
 
 }  // namespace evo
