@@ -10,10 +10,10 @@
 //
 // Two kernels, each recomputing S and P (the reductions run along different
 // axes and stay on chip without atomics):
-//   bwd_q3   64 queries of one (b, h) and a group of n per workgroup: dQ,
+//   bwd_q3   128 queries of one (b, h) and a group of n per workgroup: dQ,
 //            delta (written for bwd_kv3), and dpair summed over the n-group in
 //            registers, written once per group as an fp32 partial;
-//   bwd_kv3  64 keys of one (b, h) and a group of n per workgroup: dK, dV and
+//   bwd_kv3  128 keys of one (b, h) and a group of n per workgroup: dK, dV and
 //            the per-head dmask partials.
 // Both use v_mfma_f32_16x16x32 tiles (a wave owns 16 rows) and take as much
 // per-score work off the vector ALU as the accumulator layout allows:
@@ -30,19 +30,27 @@
 
 namespace evo {
 
-constexpr int kTileRows = 64;  // queries (bwd_q3) or keys (bwd_kv3) per workgroup
+// A workgroup has NW waves; wave w owns rows 16w..16w+15 of the workgroup's
+// 16 NW queries (bwd_q3) or keys (bwd_kv3).  Eight waves (128 rows) halve the
+// tile traffic per score against four and still keep two waves per SIMD.
+constexpr int kWaves = 8;
 
 // Per-thread byte offsets, relative to the first element of a (b, n) slice,
 // of the 16-byte chunks this thread copies into a tile (rows = keys [0, CH),
 // clamped to L - 1; K-layout chunks first, then V-layout chunks).  They do not
 // depend on n, so the per-slice copy is a base pointer plus these offsets.
-template <int D>
-__device__ __forceinline__ void tile_chunk_offsets(uint32_t (&off)[KVTile<D>::TCH / 256], int L, int H, int h, int wave,
-                                                   int lane) {
+template <int D, int NT>
+struct TileCopy {
+  static constexpr int N = (KVTile<D>::TCH + NT - 1) / NT;  // chunks per thread (the last may be partial)
+  uint32_t off[N];
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void tile_chunk_offsets(TileCopy<D, NT>& tc, int L, int H, int h, int wave, int lane) {
   using TL = KVTile<D>;
 #pragma unroll
-  for (int c = 0; c < TL::TCH / 256; ++c) {
-    const int q = wave * 64 + 256 * c + lane;
+  for (int c = 0; c < TileCopy<D, NT>::N; ++c) {
+    const int q = min(wave * 64 + NT * c + lane, TL::TCH - 1);
     int r, cc;
     if (q < TL::KCH) {
       r = q / TL::KC;
@@ -54,20 +62,21 @@ __device__ __forceinline__ void tile_chunk_offsets(uint32_t (&off)[KVTile<D>::TC
       if (cc >= D / 8) cc = 0;  // columns the transposed reads touch but never use
     }
     const int j = min(r, L - 1);
-    off[c] = (uint32_t)((((size_t)j * H + h) * D + 8 * cc) * 2);
+    tc.off[c] = (uint32_t)((((size_t)j * H + h) * D + 8 * cc) * 2);
   }
 }
 
 // Issue the asynchronous copies of one slice's tile (rows of `kx` in the K
 // layout, rows of `vx` in the V layout) into an LDS buffer.
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void issue_tile(uint8_t* buf, const uint16_t* kx, const uint16_t* vx,
-                                           const uint32_t (&off)[KVTile<D>::TCH / 256], int wave) {
+                                           const TileCopy<D, NT>& tc, int wave) {
   using TL = KVTile<D>;
 #pragma unroll
-  for (int c = 0; c < TL::TCH / 256; ++c) {
-    const int base = wave * 64 + 256 * c;
-    const char* src = reinterpret_cast<const char*>(base < TL::KCH ? kx : vx) + off[c];
+  for (int c = 0; c < TileCopy<D, NT>::N; ++c) {
+    const int base = wave * 64 + NT * c;  // wave-uniform
+    if ((TL::TCH % NT) != 0 && base >= TL::TCH) break;
+    const char* src = reinterpret_cast<const char*>(base < TL::KCH ? kx : vx) + tc.off[c];
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)(buf + base * 16), 16, 0, 0);
   }
@@ -83,22 +92,22 @@ __device__ __forceinline__ void issue_tile(uint8_t* buf, const uint16_t* kx, con
 //   P = exp2((S*scale + pair) log2e - lse log2e),  dS^T = P dP^T
 //   dQ^T += K^T dS^T                     (K^T by transposed LDS reads)
 //   dpair^T[block] += I dS^T[block]      (16x16x16 MFMA against an identity)
-template <class T, int D, bool HAS_PAIR, bool WANT_DPAIR>
-__global__ __launch_bounds__(256, 2) void evo_bwd_q3_kernel(BwdArgs a) {
+template <class T, int D, bool HAS_PAIR, bool WANT_DPAIR, int NW>
+__global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   using TL = KVTile<D>;
   constexpr int KS32 = (D + 31) / 32;  // 32-wide k-steps over d
   constexpr int NB = TL::CH / 16;      // 16-key blocks per tile
   constexpr int NSTEP = TL::CH / 32;   // 32-key steps per tile
   constexpr int MB = (D + 15) / 16;    // 16-row blocks of dQ^T
   constexpr int KC = TL::KC, VC = TL::VC;
-  constexpr int NCH = TL::TCH / 256;
+  constexpr int NT = 64 * NW, kRows = 16 * NW;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BUF_BYTES];
   __shared__ __attribute__((aligned(16))) float smk[2][TL::CH];  // sqrt(D) * mask of key j, -inf past L
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int L = a.L, H = a.H, N = a.N;
-  const int itiles = (L + kTileRows - 1) / kTileRows;
+  const int itiles = (L + kRows - 1) / kRows;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int h = wg % H;
   int rest = wg / H;
@@ -106,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_q3_kernel(BwdArgs a) {
   rest /= itiles;
   const int ng = rest % a.n_groups_q;
   const int b = rest / a.n_groups_q;
-  const int i = it * kTileRows + wave * 16 + col;
+  const int i = it * kRows + wave * 16 + col;
   const bool i_valid = i < L;
   const int ic = min(i, L - 1);
   const int n_begin = ng * a.Gq, n_end = min(N, n_begin + a.Gq);
@@ -139,8 +148,8 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_q3_kernel(BwdArgs a) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) ident[e] = (4 * g + e == col) ? T::one() : (short)0;
 
-  uint32_t coff[NCH];
-  tile_chunk_offsets<D>(coff, L, H, h, wave, lane);
+  TileCopy<D, NT> coff;
+  tile_chunk_offsets<D, NT>(coff, L, H, h, wave, lane);
 
   short8_t qop[KS32], gop[KS32], qnx[KS32], gnx[KS32], onx[KS32];
   float lse_nx = 0.f;
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_q3_kernel(BwdArgs a) {
 
   if (ntiles > 0) {
     load_rows(n_begin);
-    issue_tile<D>(smem, slice_ptr(a.k, n_begin), slice_ptr(a.v, n_begin), coff, wave);
+    issue_tile<D, NT>(smem, slice_ptr(a.k, n_begin), slice_ptr(a.v, n_begin), coff, wave);
     store_mask(0);
   }
   for (int t = 0; t < ntiles; ++t) {
@@ -206,22 +215,24 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_q3_kernel(BwdArgs a) {
     }
     const floatx4 ndel = {-del, -del, -del, -del};
     if (t + 1 < ntiles) {
-      issue_tile<D>(smem + ((t + 1) & 1) * TL::BUF_BYTES, slice_ptr(a.k, n + 1), slice_ptr(a.v, n + 1), coff, wave);
+      issue_tile<D, NT>(smem + ((t + 1) & 1) * TL::BUF_BYTES, slice_ptr(a.k, n + 1), slice_ptr(a.v, n + 1), coff, wave);
       load_rows(n + 1);
     }
     const uint8_t* kb = smem + (t & 1) * TL::BUF_BYTES;
     const uint8_t* vb = kb + TL::KCH * 16;
     const float* mkb = &smk[t & 1][4 * g];
-    // row (key) 16 blk + col of a tile: the swizzle depends on col only, so a
-    // block's operands sit at a fixed offset from the lane's base
-    const uint8_t* kbase[KS32];
-    const uint8_t* vbase[KS32];
+    // Row (key) 16 blk + col of a tile: the swizzle depends on col only, so a
+    // block's operands sit at a fixed offset from the lane's base address.
+    // For D < 32 the k-slots past D read finite tile data that meets zeros in
+    // the Q and dO operands.
+    uint32_t kaddr[KS32], vaddr[KS32];
 #pragma unroll
     for (int s = 0; s < KS32; ++s) {
       const int c = 4 * s + g;
-      kbase[s] = kb + (col * KC + ((c < KC ? c : 0) ^ kv_swz<KC>(col))) * 16;
-      vbase[s] = vb + (col * VC + ((c < VC ? c : 0) ^ kv_swz<VC>(col))) * 16;
+      kaddr[s] = lds_addr(kb + (col * KC + ((c < KC ? c : 0) ^ kv_swz<KC>(col))) * 16);
+      vaddr[s] = lds_addr(vb + (col * VC + ((c < VC ? c : 0) ^ kv_swz<VC>(col))) * 16);
     }
+    const uint32_t maddr = lds_addr(mkb);
     // transposed K^T reads: row 4g + col/4 (+32 per step, +16 for the upper
     // half), column 16 mb + 4 (col % 4); the swizzle again depends on the lane only
     uint32_t ktaddr[MB];
@@ -229,45 +240,72 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_q3_kernel(BwdArgs a) {
     for (int mb = 0; mb < MB; ++mb)
       ktaddr[mb] = lds_addr(kb) + tr_off<KC>(4 * g + (col >> 2), 16 * mb + 4 * (col & 3));
 
-    auto sblk = [&](int blk) -> floatx4 {
-      floatx4 acc = *reinterpret_cast<const floatx4*>(mkb + 16 * blk);
-#pragma unroll
-      for (int s = 0; s < KS32; ++s) {
-        short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (4 * s + g < KC) op = *reinterpret_cast<const short8_t*>(kbase[s] + blk * 16 * KC * 16);
-        acc = T::mfma16(op, qop[s], acc);
-      }
-      return acc;
+    // Operands of one 32-key step (blocks 2 st and 2 st + 1): K rows, V rows
+    // and the mask term, read one step ahead of the products that use them
+    // (the reads complete under a step of vector work).
+    struct StepOps {
+      u32x4 k[2][KS32], v[2][KS32], m[2];
     };
-    auto dpblk = [&](int blk) -> floatx4 {
-      floatx4 acc = ndel;
+    auto load_ops = [&](auto stc, StepOps& o) {
+      constexpr int st = decltype(stc)::value;
+      static_for<0, 2>([&](auto hc) {
+        constexpr int hb = decltype(hc)::value, blk = 2 * st + hb;
+        static_for<0, KS32>([&](auto sc_) {
+          constexpr int s = decltype(sc_)::value;
+          o.k[hb][s] = lds_b128_imm<blk * 16 * KC * 16>(kaddr[s]);
+          o.v[hb][s] = lds_b128_imm<blk * 16 * VC * 16>(vaddr[s]);
+        });
+        o.m[hb] = lds_b128_imm<blk * 64>(maddr);
+      });
+    };
+    auto touch_ops = [&](StepOps& o) {
 #pragma unroll
-      for (int s = 0; s < KS32; ++s) {
-        short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (4 * s + g < D / 8) op = *reinterpret_cast<const short8_t*>(vbase[s] + blk * 16 * VC * 16);
-        acc = T::mfma16(op, gop[s], acc);
+      for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+        for (int s = 0; s < KS32; ++s) {
+          reg_touch(o.k[hb][s]);
+          reg_touch(o.v[hb][s]);
+        }
+        reg_touch(o.m[hb]);
       }
-      return acc;
+    };
+    // S^T = K Q^T + sqrt(D) mask and dP^T = V dO^T - delta of one step
+    auto products = [&](const StepOps& o, floatx4(&sv)[2], floatx4(&dv)[2]) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        floatx4 acc = __builtin_bit_cast(floatx4, o.m[hb]), accd = ndel;
+#pragma unroll
+        for (int s = 0; s < KS32; ++s) {
+          acc = T::mfma16(__builtin_bit_cast(short8_t, o.k[hb][s]), qop[s], acc);
+          accd = T::mfma16(__builtin_bit_cast(short8_t, o.v[hb][s]), gop[s], accd);
+        }
+        sv[hb] = acc;
+        dv[hb] = accd;
+      }
     };
 
     floatx4 dq[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) dq[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
     floatx4 sc[2][2], dp[2][2];
-    sc[0][0] = sblk(0);
-    sc[0][1] = sblk(1);
-    dp[0][0] = dpblk(0);
-    dp[0][1] = dpblk(1);
+    StepOps ops;
+    load_ops(std::integral_constant<int, 0>{}, ops);
+    lgkm_wait<0>();
+    touch_ops(ops);
+    products(ops, sc[0], dp[0]);
+    if constexpr (NSTEP > 1) load_ops(std::integral_constant<int, 1>{}, ops);
     static_for<0, NSTEP>([&](auto stc) {
       constexpr int st = decltype(stc)::value;
       constexpr int cur = st & 1;
-      // the next step's products are issued before this step's vector work
-      // (rows past L read finite tile data and are never used)
+      // The next step's products are issued before this step's vector work
+      // (their operands were read during the previous step), and the
+      // operands of the step after are read.  Rows past L read finite tile
+      // data and are never used.
       if constexpr (st + 1 < NSTEP) {
-        sc[cur ^ 1][0] = sblk(2 * st + 2);
-        sc[cur ^ 1][1] = sblk(2 * st + 3);
-        dp[cur ^ 1][0] = dpblk(2 * st + 2);
-        dp[cur ^ 1][1] = dpblk(2 * st + 3);
+        lgkm_wait<0>();
+        touch_ops(ops);
+        products(ops, sc[cur ^ 1], dp[cur ^ 1]);
+        if constexpr (st + 2 < NSTEP) load_ops(std::integral_constant<int, st + 2>{}, ops);
       }
       if (32 * st < L) {
         short4_t kt[2 * MB];  // [mb][lo/hi 16 keys]
@@ -276,6 +314,8 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_q3_kernel(BwdArgs a) {
           kt[2 * mb] = lds_tr_imm<st * 32 * KC * 16>(ktaddr[mb]);
           kt[2 * mb + 1] = lds_tr_imm<st * 32 * KC * 16 + 16 * KC * 16>(ktaddr[mb]);
         }
+        // keep the vector work below the reads so that it covers their latency
+        __builtin_amdgcn_sched_barrier(0);
         float ds[2][4];
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
@@ -300,7 +340,9 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_q3_kernel(BwdArgs a) {
           dpacc[2 * st] = T::mfma16k16(ident, __builtin_bit_cast(short4_t, u32x2{dw[0], dw[1]}), dpacc[2 * st]);
           dpacc[2 * st + 1] = T::mfma16k16(ident, __builtin_bit_cast(short4_t, u32x2{dw[2], dw[3]}), dpacc[2 * st + 1]);
         }
-        lds_wait_all(kt);
+        lgkm_wait<0>();
+#pragma unroll
+        for (int k = 0; k < 2 * MB; ++k) reg_touch(kt[k]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) dq[mb] = T::mfma16(cat4(kt[2 * mb], kt[2 * mb + 1]), dsb, dq[mb]);
       }
@@ -342,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_q3_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- bwd_kv3
 //
-// The mirror image: wave w owns keys 16w..16w+15 of the workgroup's 64 (lane
+// The mirror image: wave w owns keys 16w..16w+15 of the workgroup's 16 NW (lane
 // = key, S layout with query rows); K and V rows of the lane's key are the
 // MFMA B operands; per n the Q and dO rows of the slice arrive in LDS
 // (same tile layout), -lse log2e and -delta per query through LDS.  Per
@@ -352,18 +394,18 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_q3_kernel(BwdArgs a) {
 //   P = exp2(...),  dS = P dP
 //   dV^T += dO^T P,  dK^T += Q^T dS      (dO^T, Q^T by transposed LDS reads)
 //   dmask partial += column sums of dS   (MFMA against a row of ones)
-// The pair-bias columns of the 64 keys are read once per workgroup (through
+// The pair-bias columns of the workgroup's keys are read once per workgroup (through
 // LDS, transposed) and stay in registers for the whole n-group.
-template <class T, int D, bool HAS_PAIR, bool WANT_DMASK>
-__global__ __launch_bounds__(256, 2) void evo_bwd_kv3_kernel(BwdArgs a) {
+template <class T, int D, bool HAS_PAIR, bool WANT_DMASK, int NW>
+__global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   using TL = KVTile<D>;
   constexpr int KS32 = (D + 31) / 32;
   constexpr int NB = TL::CH / 16;  // 16-query blocks per tile
   constexpr int NSTEP = TL::CH / 32;
   constexpr int MB = (D + 15) / 16;
   constexpr int KC = TL::KC, VC = TL::VC;
-  constexpr int NCH = TL::TCH / 256;
-  constexpr int kSlab = HAS_PAIR ? TL::CH * kTileRows * 2 : 0;  // pair[:, 64 keys] staged once
+  constexpr int NT = 64 * NW, kRows = 16 * NW;
+  constexpr int kSlab = HAS_PAIR ? TL::CH * kRows * 2 : 0;  // pair[:, the workgroup's keys] staged once
   constexpr int kSmem = 2 * TL::BUF_BYTES > kSlab ? 2 * TL::BUF_BYTES : kSlab;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   __shared__ __attribute__((aligned(16))) float slse[2][TL::CH];  // -lse log2e; -inf past L / no finite score
@@ -372,7 +414,7 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_kv3_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int L = a.L, H = a.H, N = a.N;
-  const int jtiles = (L + kTileRows - 1) / kTileRows;
+  const int jtiles = (L + kRows - 1) / kRows;
   const int ngroups = (N + a.Gq - 1) / a.Gq;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int h = wg % H;
@@ -381,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_kv3_kernel(BwdArgs a) {
   rest /= jtiles;
   const int ng = rest % ngroups;
   const int b = rest / ngroups;
-  const int j = jt * kTileRows + wave * 16 + col;  // this lane's key
+  const int j = jt * kRows + wave * 16 + col;  // this lane's key
   const bool j_valid = j < L;
   const int jc = min(j, L - 1);
   const int n_begin = ng * a.Gq, n_end = min(N, n_begin + a.Gq);
@@ -393,12 +435,13 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_kv3_kernel(BwdArgs a) {
   if constexpr (HAS_PAIR) {
     const uint16_t* pbase = a.pair + ((size_t)b * H + h) * L * L;
     if ((L % 8) == 0) {
-      // stage pair[0..L)[64 keys] row-major (128-byte rows) with 16-byte
-      // copies, then read columns with transposed reads
-      const int kc0 = jt * kTileRows;
-      for (int base = wave * 64; base < TL::CH * 8; base += 256) {
+      // stage pair[0..L)[the workgroup's keys] row-major (2 kRows-byte rows)
+      // with 16-byte copies, then read columns with transposed reads
+      constexpr int RC = kRows / 8;  // 16-byte chunks per slab row
+      const int kc0 = jt * kRows;
+      for (int base = wave * 64; base < TL::CH * RC; base += NT) {
         const int q = base + lane;
-        const int r = q >> 3, c = q & 7;
+        const int r = q / RC, c = q % RC;
         const uint16_t* src = pbase + (size_t)min(r, L - 1) * L + min(kc0 + 8 * c, L - 8);
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                          (__attribute__((address_space(3))) void*)(smem + base * 16), 16, 0, 0);
@@ -409,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_kv3_kernel(BwdArgs a) {
       for (int qb = 0; qb < NB; ++qb) {
         const int row = 16 * qb + 4 * g + (col >> 2);
         const int kcol = wave * 16 + 4 * (col & 3);
-        const short4_t v = lds_read_tr_b(smem, (row * kTileRows + kcol) * 2);
+        const short4_t v = lds_read_tr_b(smem, (row * kRows + kcol) * 2);
         pbias[qb] = __builtin_bit_cast(u32x2, v);
       }
       __syncthreads();
@@ -433,8 +476,8 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_kv3_kernel(BwdArgs a) {
     for (int e = 0; e < 8; ++e) ones[e] = T::one();
   }
 
-  uint32_t coff[NCH];
-  tile_chunk_offsets<D>(coff, L, H, h, wave, lane);
+  TileCopy<D, NT> coff;
+  tile_chunk_offsets<D, NT>(coff, L, H, h, wave, lane);
 
   // ---- per-slice key operands (B of S = Q K^T and dP = dO V^T): lane = key
   short8_t kop[KS32], vop[KS32], knx[KS32], vnx[KS32];
@@ -472,7 +515,7 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_kv3_kernel(BwdArgs a) {
 
   if (ntiles > 0) {
     load_keys(n_begin);
-    issue_tile<D>(smem, slice_ptr(a.q, n_begin), slice_ptr(a.dout, n_begin), coff, wave);
+    issue_tile<D, NT>(smem, slice_ptr(a.q, n_begin), slice_ptr(a.dout, n_begin), coff, wave);
     store_rows(0);
   }
   for (int t = 0; t < ntiles; ++t) {
@@ -488,21 +531,21 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_kv3_kernel(BwdArgs a) {
     const float mk = j_valid ? T::to_f32((uint16_t)mnx) * a.sqrt_d : kNegInf;
     const floatx4 mk4 = {mk, mk, mk, mk};
     if (t + 1 < ntiles) {
-      issue_tile<D>(smem + ((t + 1) & 1) * TL::BUF_BYTES, slice_ptr(a.q, n + 1), slice_ptr(a.dout, n + 1), coff, wave);
+      issue_tile<D, NT>(smem + ((t + 1) & 1) * TL::BUF_BYTES, slice_ptr(a.q, n + 1), slice_ptr(a.dout, n + 1), coff,
+                        wave);
       load_keys(n + 1);
     }
     const uint8_t* qb_ = smem + (t & 1) * TL::BUF_BYTES;
     const uint8_t* ob_ = qb_ + TL::KCH * 16;
-    const float* lrow = &slse[t & 1][4 * g];
-    const float* drow = &sndel[t & 1][4 * g];
-    const uint8_t* qbase[KS32];
-    const uint8_t* obase[KS32];
+    // per-lane LDS byte addresses (see bwd_q3)
+    uint32_t qaddr[KS32], oaddr[KS32];
 #pragma unroll
     for (int s = 0; s < KS32; ++s) {
       const int c = 4 * s + g;
-      qbase[s] = qb_ + (col * KC + ((c < KC ? c : 0) ^ kv_swz<KC>(col))) * 16;
-      obase[s] = ob_ + (col * VC + ((c < VC ? c : 0) ^ kv_swz<VC>(col))) * 16;
+      qaddr[s] = lds_addr(qb_ + (col * KC + ((c < KC ? c : 0) ^ kv_swz<KC>(col))) * 16);
+      oaddr[s] = lds_addr(ob_ + (col * VC + ((c < VC ? c : 0) ^ kv_swz<VC>(col))) * 16);
     }
+    const uint32_t laddr = lds_addr(&slse[t & 1][4 * g]), daddr = lds_addr(&sndel[t & 1][4 * g]);
     uint32_t qtaddr[MB], otaddr[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -510,25 +553,55 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_kv3_kernel(BwdArgs a) {
       otaddr[mb] = lds_addr(ob_) + tr_off<VC>(4 * g + (col >> 2), 16 * mb + 4 * (col & 3));
     }
 
-    auto sblk = [&](int blk) -> floatx4 {
-      floatx4 acc = mk4;
-#pragma unroll
-      for (int s = 0; s < KS32; ++s) {
-        short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (4 * s + g < KC) op = *reinterpret_cast<const short8_t*>(qbase[s] + blk * 16 * KC * 16);
-        acc = T::mfma16(op, kop[s], acc);
-      }
-      return acc;
+    // Operands of one 32-query step (blocks 2 st, 2 st + 1): Q rows, dO rows,
+    // -delta and -lse log2e of the block's queries, read one step ahead of
+    // the products.  -lse log2e is consumed by the vector work a step later,
+    // so it rotates through three slots.
+    struct StepOps {
+      u32x4 q[2][KS32], o[2][KS32], d[2];
     };
-    auto dpblk = [&](int blk) -> floatx4 {
-      floatx4 acc = *reinterpret_cast<const floatx4*>(drow + 16 * blk);
+    u32x4 nlr[3][2];
+    auto load_ops = [&](auto stc, StepOps& o) {
+      constexpr int st = decltype(stc)::value;
+      static_for<0, 2>([&](auto hc) {
+        constexpr int hb = decltype(hc)::value, blk = 2 * st + hb;
+        static_for<0, KS32>([&](auto sc_) {
+          constexpr int s = decltype(sc_)::value;
+          o.q[hb][s] = lds_b128_imm<blk * 16 * KC * 16>(qaddr[s]);
+          o.o[hb][s] = lds_b128_imm<blk * 16 * VC * 16>(oaddr[s]);
+        });
+        o.d[hb] = lds_b128_imm<blk * 64>(daddr);
+        nlr[st % 3][hb] = lds_b128_imm<blk * 64>(laddr);
+      });
+    };
+    auto touch_ops = [&](StepOps& o, int slot) {
 #pragma unroll
-      for (int s = 0; s < KS32; ++s) {
-        short8_t op = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (4 * s + g < D / 8) op = *reinterpret_cast<const short8_t*>(obase[s] + blk * 16 * VC * 16);
-        acc = T::mfma16(op, vop[s], acc);
+      for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+        for (int s = 0; s < KS32; ++s) {
+          reg_touch(o.q[hb][s]);
+          reg_touch(o.o[hb][s]);
+        }
+        reg_touch(o.d[hb]);
       }
-      return acc;
+      // slot is a compile-time constant at every call
+      if (slot == 0) { reg_touch(nlr[0][0]); reg_touch(nlr[0][1]); }
+      if (slot == 1) { reg_touch(nlr[1][0]); reg_touch(nlr[1][1]); }
+      if (slot == 2) { reg_touch(nlr[2][0]); reg_touch(nlr[2][1]); }
+    };
+    // S = Q K^T + sqrt(D) mask_j and dP = dO V^T - delta_i of one step
+    auto products = [&](const StepOps& o, floatx4(&sv)[2], floatx4(&dv)[2]) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        floatx4 acc = mk4, accd = __builtin_bit_cast(floatx4, o.d[hb]);
+#pragma unroll
+        for (int s = 0; s < KS32; ++s) {
+          acc = T::mfma16(__builtin_bit_cast(short8_t, o.q[hb][s]), kop[s], acc);
+          accd = T::mfma16(__builtin_bit_cast(short8_t, o.o[hb][s]), vop[s], accd);
+        }
+        sv[hb] = acc;
+        dv[hb] = accd;
+      }
     };
 
     floatx4 dk[MB], dv[MB], dmk = {0.f, 0.f, 0.f, 0.f};
@@ -538,18 +611,20 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_kv3_kernel(BwdArgs a) {
       dv[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
     floatx4 sc[2][2], dp[2][2];
-    sc[0][0] = sblk(0);
-    sc[0][1] = sblk(1);
-    dp[0][0] = dpblk(0);
-    dp[0][1] = dpblk(1);
+    StepOps ops;
+    load_ops(std::integral_constant<int, 0>{}, ops);
+    lgkm_wait<0>();
+    touch_ops(ops, 0);
+    products(ops, sc[0], dp[0]);
+    if constexpr (NSTEP > 1) load_ops(std::integral_constant<int, 1>{}, ops);
     static_for<0, NSTEP>([&](auto stc) {
       constexpr int st = decltype(stc)::value;
       constexpr int cur = st & 1;
       if constexpr (st + 1 < NSTEP) {
-        sc[cur ^ 1][0] = sblk(2 * st + 2);
-        sc[cur ^ 1][1] = sblk(2 * st + 3);
-        dp[cur ^ 1][0] = dpblk(2 * st + 2);
-        dp[cur ^ 1][1] = dpblk(2 * st + 3);
+        lgkm_wait<0>();
+        touch_ops(ops, (st + 1) % 3);
+        products(ops, sc[cur ^ 1], dp[cur ^ 1]);
+        if constexpr (st + 2 < NSTEP) load_ops(std::integral_constant<int, st + 2>{}, ops);
       }
       if (32 * st < L) {
         short4_t tt[4 * MB];  // [mb][q lo, q hi, o lo, o hi]
@@ -560,11 +635,13 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_kv3_kernel(BwdArgs a) {
           tt[4 * mb + 2] = lds_tr_imm<st * 32 * VC * 16>(otaddr[mb]);
           tt[4 * mb + 3] = lds_tr_imm<st * 32 * VC * 16 + 16 * VC * 16>(otaddr[mb]);
         }
+        // keep the vector work below the reads so that it covers their latency
+        __builtin_amdgcn_sched_barrier(0);
         float pv[2][4], ds[2][4];
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
           const int blk = 2 * st + hb;
-          const floatx4 nl4 = *reinterpret_cast<const floatx4*>(lrow + 16 * blk);
+          const floatx4 nl4 = __builtin_bit_cast(floatx4, nlr[st % 3][hb]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float x;
@@ -587,7 +664,9 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_kv3_kernel(BwdArgs a) {
             short8_t, u32x4{T::pack2(ds[0][0], ds[0][1]), T::pack2(ds[0][2], ds[0][3]), T::pack2(ds[1][0], ds[1][1]),
                             T::pack2(ds[1][2], ds[1][3])});
         if constexpr (WANT_DMASK) dmk = T::mfma16(ones, db, dmk);
-        lds_wait_all(tt);
+        lgkm_wait<0>();
+#pragma unroll
+        for (int k = 0; k < 4 * MB; ++k) reg_touch(tt[k]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           dk[mb] = T::mfma16(cat4(tt[4 * mb], tt[4 * mb + 1]), db, dk[mb]);
@@ -624,19 +703,20 @@ static hipError_t launch_tile_t(const BwdArgs& a, hipStream_t st) {
   const bool want_dmask = a.dmask != nullptr;
   const bool want_dpair = a.dpair != nullptr;
   // bwd_q3 forms delta and leaves it in the workspace for bwd_kv3
-  const int gridq = a.B * a.H * ((a.L + kTileRows - 1) / kTileRows) * a.n_groups_q;
+  constexpr int NW = kWaves, kRows = 16 * kWaves;
+  const int gridq = a.B * a.H * ((a.L + kRows - 1) / kRows) * a.n_groups_q;
   prof_begin(K_BWD_Q, st);
   if (want_dpair)
-    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, true>), dim3(gridq), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, true, NW>), dim3(gridq), dim3(64 * NW), 0, st, a);
   else
-    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, false>), dim3(gridq), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, false, NW>), dim3(gridq), dim3(64 * NW), 0, st, a);
   prof_end(K_BWD_Q, st);
-  const int gridk = a.B * a.H * ((a.L + kTileRows - 1) / kTileRows) * ((a.N + a.Gq - 1) / a.Gq);
+  const int gridk = a.B * a.H * ((a.L + kRows - 1) / kRows) * ((a.N + a.Gq - 1) / a.Gq);
   prof_begin(K_BWD_KV, st);
   if (want_dmask)
-    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, true>), dim3(gridk), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, true, NW>), dim3(gridk), dim3(64 * NW), 0, st, a);
   else
-    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, false>), dim3(gridk), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, false, NW>), dim3(gridk), dim3(64 * NW), 0, st, a);
   prof_end(K_BWD_KV, st);
   return hipGetLastError();
 }

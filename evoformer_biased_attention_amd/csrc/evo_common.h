@@ -333,4 +333,29 @@ __device__ __forceinline__ short4_t lds_tr_imm(uint32_t addr) {
   return __builtin_bit_cast(short4_t, r);
 }
 
+// 16-byte LDS read at a compile-time byte offset, not tracked by the
+// compiler (see lds_read_tr_asm): wait with lgkm_wait() and mark the result
+// with reg_touch() before using it.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_b128_imm(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// Wait until at most N LDS (and scalar-memory) operations are outstanding.
+// LDS reads complete in issue order, so this waits for every LDS read issued
+// before the last N of them, whatever scalar loads are also in flight.
+template <int N>
+__device__ __forceinline__ void lgkm_wait() {
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N) : "memory");
+}
+// Make a register value an output of an (empty) asm placed after a wait, so
+// that no use of it is scheduled before the wait.
+template <class R>
+__device__ __forceinline__ void reg_touch(R& r) {
+  asm volatile("" : "+v"(r));
+}
+
 }  // namespace evo
