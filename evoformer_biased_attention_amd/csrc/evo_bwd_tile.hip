@@ -181,6 +181,21 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   floatx4 dpacc[WANT_DPAIR ? NB : 1];
 #pragma unroll
   for (int blk = 0; blk < (WANT_DPAIR ? NB : 1); ++blk) dpacc[blk] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // the group's fp32 dpair partial of block blk (keys 16 blk + 4 g + 0..3 of query i)
+  float* const dpdst = WANT_DPAIR ? a.dpair_part + ((((size_t)ng * a.B + b) * H + h) * L + ic) * L : nullptr;
+  auto store_dpair = [&](int blk) {
+    if constexpr (WANT_DPAIR) {
+      if (!i_valid) return;
+      const int j = 16 * blk + 4 * g;
+      if (j + 4 <= L && (L % 4) == 0) {
+        *reinterpret_cast<floatx4*>(dpdst + j) = dpacc[blk];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (j + u < L) dpdst[j + u] = dpacc[blk][u];
+      }
+    }
+  };
 
   if (ntiles > 0) {
     load_rows(n_begin);
@@ -307,6 +322,14 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
         products(ops, sc[cur ^ 1], dp[cur ^ 1]);
         if constexpr (st + 2 < NSTEP) load_ops(std::integral_constant<int, st + 2>{}, ops);
       }
+      // in the group's last slice, blocks are final once their step is done:
+      // their stores overlap the remaining steps
+      if constexpr (WANT_DPAIR && st >= 1) {
+        if (t + 1 == ntiles) {
+          store_dpair(2 * st - 2);
+          store_dpair(2 * st - 1);
+        }
+      }
       if (32 * st < L) {
         short4_t kt[2 * MB];  // [mb][lo/hi 16 keys]
 #pragma unroll
@@ -365,19 +388,9 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   }
 
   if constexpr (WANT_DPAIR) {
-    if (i_valid) {
-      float* dst = a.dpair_part + ((((size_t)ng * a.B + b) * H + h) * L + i) * L;
-#pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        const int j = 16 * blk + 4 * g;
-        if (j + 4 <= L && (L % 4) == 0) {
-          *reinterpret_cast<floatx4*>(dst + j) = dpacc[blk];
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (j + u < L) dst[j + u] = dpacc[blk][u];
-        }
-      }
+    if (ntiles > 0) {
+      store_dpair(NB - 2);
+      store_dpair(NB - 1);
     }
   }
 }
