@@ -102,7 +102,7 @@ def parse_traffic(fetch_dir, write_dir, workload):
         return expect / max(cands) if cands else 1.0
 
     fs, ws = calib(fetch, COPY_BYTES), calib(write, COPY_BYTES)
-    kinds = {"evo_fwd_kernel": "fwd", "evo_bwd_q2_kernel": "bwd_q", "evo_bwd_kv2_kernel": "bwd_kv",
+    kinds = {"evo_fwd_kernel": "fwd", "evo_bwd_q3_kernel": "bwd_q", "evo_bwd_kv3_kernel": "bwd_kv",
              "evo_bwd_fin_kernel": "bwd_fin", "evo_bwd_q_kernel": "bwd_q", "evo_bwd_kv_kernel": "bwd_kv",
              "evo_bwd_pre_kernel": "bwd_pre"}
     sha = kernel_sources_sha()
