@@ -10,6 +10,7 @@
 
 #include <cmath>
 #include <cstdlib>
+#include <climits>
 #include <cstring>
 #include <mutex>
 
@@ -17,6 +18,7 @@
 #include "evo_kernels.h"
 #include "evo_prof.h"
 
+#include <algorithm>
 #include <atomic>
 #include <vector>
 
@@ -160,20 +162,29 @@ int plan_fwd_group(const Shape& s) {
   return env_int("EVOATTN_FWD_G", (int)g);
 }
 
-// slices per bwd_q workgroup (also the dpair partial count divisor): about
-// 1024 workgroups; the kernels for rows longer than one key tile keep their
-// query tile small, so their groups stop at 8 (measured on MI355X)
+// keys per backward tile (KVTile<D>::CH)
+int64_t key_tile(int64_t D) { return D == 64 ? 128 : 256; }
+
+// slices per bwd_q3 / bwd_kv3 workgroup (also the dpair partial count
+// divisor).  A workgroup takes 128 rows and one key tile; one runs per CU
+// (256 CUs).  The group count k is the smallest within 3% of the minimum of
+// (rounds of workgroups) x (slices per workgroup): fewer groups mean fewer
+// dpair partials and fewer per-workgroup set-ups.
 int plan_bwdq_group(const Shape& s) {
-  const int64_t base = s.B * s.H * ((s.L + 31) / 32);
-  int64_t g = (s.N * base) / 1024;
-  if (s.L > (s.D == 64 ? 128 : 256) && g > 8) g = 8;
-  if (g < 1) g = 1;
-  if (g > s.N) g = s.N;
+  const int64_t jtiles = (s.L + key_tile(s.D) - 1) / key_tile(s.D);
+  const int64_t per_group = s.B * s.H * ((s.L + 127) / 128) * jtiles;
+  const int64_t kmax = s.N < 4096 ? s.N : 4096;
+  auto cost = [&](int64_t k) { return ((per_group * k + 255) / 256) * ((s.N + k - 1) / k); };
+  int64_t best_t = INT64_MAX;
+  for (int64_t k = 1; k <= kmax; ++k) best_t = std::min(best_t, cost(k));
+  int64_t k = 1;
+  while (k < kmax && cost(k) * 100 > best_t * 103) ++k;
+  const int64_t g = (s.N + k - 1) / k;
   return env_int("EVOATTN_BWD_GQ", (int)g);
 }
 
 struct WsLayout {
-  size_t delta, dmask_part, dmask_f32, dpair_part, dpair_f32, total;
+  size_t delta, dmask_part, dmask_f32, dpair_part, dpair_f32, dq_part, total;
   int gq, ngq;
 };
 
@@ -200,6 +211,13 @@ WsLayout ws_layout(const Shape& s, bool has_mask, bool has_pair) {
     off += al(per * (size_t)w.ngq);
     w.dpair_f32 = off;
     off += al(per);
+  }
+  // fp32 partials of dQ, one per key tile, when a row spans several tiles
+  w.dq_part = (size_t)-1;
+  const int64_t jtiles = (s.L + key_tile(s.D) - 1) / key_tile(s.D);
+  if (jtiles > 1) {
+    w.dq_part = off;
+    off += al((size_t)jtiles * s.B * s.N * s.L * s.H * s.D * sizeof(float));
   }
   w.total = off;
   return w;
@@ -389,6 +407,7 @@ evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const voi
   a.dmask_f32 = has_mask ? reinterpret_cast<float*>(ws + w.dmask_f32) : nullptr;
   a.dpair_part = has_pair ? reinterpret_cast<float*>(ws + w.dpair_part) : nullptr;
   a.dpair_f32 = has_pair ? reinterpret_cast<float*>(ws + w.dpair_f32) : nullptr;
+  a.dq_part = (w.dq_part != (size_t)-1) ? reinterpret_cast<float*>(ws + w.dq_part) : nullptr;
   a.B = (int)s.B;
   a.N = (int)s.N;
   a.L = (int)s.L;

@@ -11,27 +11,22 @@
 //   dmask[b,n,j] = sum_h sum_i dS,  dpair[b,h,i,j] = sum_n dS
 //
 // The reductions pull in different directions (dK, dV over queries; dQ over
-// keys; dpair over n; dmask over heads and queries), so the work is split:
-//   bwd_pre  delta = rowsum(dO * O), one thread per row.
+// keys; dpair over n; dmask over heads and queries), so the work is split
+// over two kernels that each recompute P, plus one reduction kernel.  Rows
+// that fit one key tile use bwd_q3 and bwd_kv3 (evo_bwd_tile.hip).  Longer
+// rows use bwd_q3 with one key tile per workgroup (dQ as fp32 partials) and
+// the key-side kernel of this file:
 //   bwd_kv   a workgroup owns 128 keys of one (b, n, h) (32 per wave) and
 //            walks all queries: dK, dV and per-head dmask partials stay in
 //            registers.  Operands: S = Q K^T with a lane per key.
-//   bwd_q    a workgroup owns 32 queries of one (b, h) and a group of n; its
-//            4 waves split the keys.  dQ is summed over the waves in LDS per
-//            n; dpair is summed over the n of the group in registers and
-//            written once per group as an fp32 partial.  Operands:
-//            S^T = K Q^T with a lane per query.
-//   bwd_fin  dmask = sum_h partials, dpair = sum_g partials, both in a fixed
-//            order (bitwise reproducible), then rounded to dtype.
-// Both bwd_kv and bwd_q recompute P from lse; that costs one extra QK^T and
-// exp per score but keeps every reduction on chip and free of atomics.
+//   bwd_fin  dmask = sum_h partials, dpair = sum_g partials, dQ = sum of the
+//            key-tile partials, each in a fixed order (bitwise
+//            reproducible), then rounded to dtype.
 #include "evo_common.h"
 #include "evo_kernels.h"
 #include "evo_prof.h"
 
 namespace evo {
-
-constexpr float kLn2 = 0.6931471805599453f;
 
 template <int D, bool HAS_MASK>
 struct BwdShape {
@@ -67,30 +62,6 @@ __device__ __forceinline__ short8_t load_row8(const uint16_t* row, int c, bool v
 __device__ __forceinline__ uint16_t pick16b(const u32x2 (&b)[4], int r) {
   uint32_t w = b[r / 4][(r % 4) / 2];
   return (r & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
-}
-
-// ---------------------------------------------------------------- bwd_pre
-
-template <class T, int D>
-__global__ __launch_bounds__(256) void evo_bwd_pre_kernel(BwdArgs a) {
-  const int64_t rows = (int64_t)a.B * a.N * a.L * a.H;
-  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
-  const int h = (int)(r % a.H);
-  const int64_t t = r / a.H;
-  const int i = (int)(t % a.L);
-  const int64_t bn = t / a.L;
-  const uint16_t* o = a.out + r * D;
-  const uint16_t* g = a.dout + r * D;
-  float s = 0.f;
-#pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    short8_t ov = *reinterpret_cast<const short8_t*>(o + c);
-    short8_t gv = *reinterpret_cast<const short8_t*>(g + c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s = __builtin_fmaf(T::to_f32((uint16_t)ov[e]), T::to_f32((uint16_t)gv[e]), s);
-  }
-  a.delta[(bn * a.H + h) * a.L + i] = s;
 }
 
 // ----------------------------------------------------------------- bwd_kv
@@ -288,257 +259,47 @@ __global__ __launch_bounds__(256, 2) void evo_bwd_kv_kernel(BwdArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ bwd_q
-
-constexpr int kQWaves = 4;
-constexpr int kQChunk = 32 * kQWaves;  // keys staged per step; wave w takes block w
-
-template <class T, int D, bool HAS_MASK, bool HAS_PAIR, bool WANT_DPAIR, int DPC>
-__global__ __launch_bounds__(256, 2) void evo_bwd_q_kernel(BwdArgs a) {
-  using S = BwdShape<D, HAS_MASK>;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kQChunk * S::KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kQChunk * S::DS];
-  __shared__ __attribute__((aligned(16))) float sRed[kQWaves * 32 * S::MB * 32];  // dQ^T partials of the 4 waves
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-  const int L = a.L, H = a.H, N = a.N;
-  const int iblocks = (L + 31) / 32;
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = wg % H;
-  int rest = wg / H;
-  const int ib = rest % iblocks;
-  rest /= iblocks;
-  const int ng = rest % a.n_groups_q;
-  const int b = rest / a.n_groups_q;
-  const int i = ib * 32 + (lane & 31);
-  const bool i_valid = i < L;
-  const int n_begin = ng * a.Gq, n_end = min(N, n_begin + a.Gq);
-  const int nchunks = (L + kQChunk - 1) / kQChunk;
-
-  floatx16 dpacc[DPC > 0 ? DPC : 1];
-#pragma unroll
-  for (int c = 0; c < (DPC > 0 ? DPC : 1); ++c) dpacc[c] = floatx16{};
-
-  const uint16_t* prow = nullptr;
-  if constexpr (HAS_PAIR) prow = a.pair + (((size_t)b * H + h) * L + (i_valid ? i : 0)) * L;
-  const bool pvec = (L % 4) == 0;
-
-  for (int n = n_begin; n < n_end; ++n) {
-    const size_t slice = ((size_t)b * N + n) * L;
-    short8_t qop[S::KSTEPS], gop[S::KSTEPS_D];
-    {
-      const uint16_t* qrow = a.q + ((slice + (i_valid ? i : 0)) * H + h) * D;
-      const uint16_t* grow = a.dout + ((slice + (i_valid ? i : 0)) * H + h) * D;
-#pragma unroll
-      for (int s = 0; s < S::KSTEPS; ++s)
-        qop[s] = load_row8<D>(qrow, 16 * s + 8 * half, i_valid, HAS_MASK, a.s_hi, a.s_lo);
-#pragma unroll
-      for (int s = 0; s < S::KSTEPS_D; ++s) gop[s] = load_row8<D>(grow, 16 * s + 8 * half, i_valid, false, 0, 0);
-    }
-    float nl = kNegInf, del = 0.f;
-    if (i_valid) {
-      const size_t ri = (((size_t)b * N + n) * H + h) * L + i;
-      float lse = a.lse[ri];
-      nl = (lse == kNegInf) ? kNegInf : -lse * kLog2e;
-      del = a.delta[ri];
-    }
-    floatx16 dq[S::MB];
-#pragma unroll
-    for (int mb = 0; mb < S::MB; ++mb) dq[mb] = floatx16{};
-
-#pragma unroll
-    for (int cu = 0; cu < (DPC > 0 ? DPC : 1); ++cu) {
-      for (int c = (DPC > 0 ? cu : 0); c < (DPC > 0 ? cu + 1 : nchunks); ++c) {
-        if (c >= nchunks) break;
-        const int kc0 = c * kQChunk;
-        __syncthreads();
-        // ---- stage K' (with mask columns) and V rows of this chunk
-        for (int t = tid; t < kQChunk * (S::KW / 8); t += 256) {
-          int r = t / (S::KW / 8), c8 = t % (S::KW / 8);
-          int jj = kc0 + r;
-          const uint16_t* krow = a.k + ((slice + (jj < L ? jj : 0)) * H + h) * D;
-          uint16_t m = 0;
-          if constexpr (HAS_MASK) m = (jj < L) ? a.mask[((size_t)b * N + n) * L + jj] : (uint16_t)0;
-          *reinterpret_cast<short8_t*>(&sK[r * S::KS + c8 * 8]) =
-              load_row8<D>(krow, c8 * 8, jj < L, HAS_MASK, m, a.s_lo != 0 ? m : (uint16_t)0);
-        }
-        for (int t = tid; t < kQChunk * (S::RW / 8); t += 256) {
-          int r = t / (S::RW / 8), c8 = t % (S::RW / 8);
-          int jj = kc0 + r;
-          short8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-          if (jj < L && c8 * 8 < D) v = *reinterpret_cast<const short8_t*>(a.v + ((slice + jj) * H + h) * D + c8 * 8);
-          *reinterpret_cast<short8_t*>(&sV[r * S::DS + c8 * 8]) = v;
-        }
-        __syncthreads();
-        const int j0 = kc0 + wave * 32;
-        if (j0 < L) {
-          // ---- S^T = K' Q'^T and dP^T = V dO^T (lane = query i)
-          floatx16 acc = floatx16{}, dp = floatx16{};
-#pragma unroll
-          for (int s = 0; s < S::KSTEPS; ++s) {
-            short8_t ka = *reinterpret_cast<const short8_t*>(&sK[(wave * 32 + (lane & 31)) * S::KS + 16 * s + 8 * half]);
-            acc = T::mfma(ka, qop[s], acc);
-          }
-#pragma unroll
-          for (int s = 0; s < S::KSTEPS_D; ++s) {
-            short8_t va = *reinterpret_cast<const short8_t*>(&sV[(wave * 32 + (lane & 31)) * S::DS + 16 * s + 8 * half]);
-            dp = T::mfma(va, gop[s], dp);
-          }
-          float sv[16];
-          if constexpr (HAS_PAIR) {
-            u32x2 pb[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              int jj = j0 + 8 * q + 4 * half;
-              u32x2 v = {0u, 0u};
-              if (i_valid) {
-                if (pvec && jj + 4 <= L) {
-                  v = *reinterpret_cast<const u32x2*>(prow + jj);
-                } else {
-                  uint16_t tt[4];
-#pragma unroll
-                  for (int u = 0; u < 4; ++u) tt[u] = (jj + u < L) ? prow[jj + u] : (uint16_t)0;
-                  v[0] = (uint32_t)tt[0] | ((uint32_t)tt[1] << 16);
-                  v[1] = (uint32_t)tt[2] | ((uint32_t)tt[3] << 16);
-                }
-              }
-              pb[q] = v;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sv[r] = T::fma_mix(acc[r], a.scale, pick16b(pb, r));
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sv[r] = acc[r] * a.scale;
-          }
-          uint32_t dspk[8];
-          float ds[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int jj = j0 + 8 * (r / 4) + 4 * half + (r % 4);
-            float p = (nl == kNegInf || jj >= L) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], kLog2e, nl));
-            ds[r] = p * (dp[r] - del);
-          }
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) dspk[r / 2] = T::pack2(ds[r], ds[r + 1]);
-          if constexpr (WANT_DPAIR && DPC > 0) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dpacc[cu][r] += ds[r];
-          } else if constexpr (WANT_DPAIR) {
-            // long rows: accumulate straight into the fp32 result (order not fixed)
-            if (i_valid) {
-              float* dst = a.dpair_f32 + (((size_t)b * H + h) * L + i) * L;
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int jj = j0 + 8 * (r / 4) + 4 * half + (r % 4);
-                if (jj < L) atomicAdd(dst + jj, ds[r]);
-              }
-            }
-          }
-          // ---- dQ^T += K^T dS^T  (A = K^T by transposed reads, k = key as held)
-          const int qg = lane >> 4, i16 = lane & 15, g = qg >> 1;
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            short8_t db = __builtin_bit_cast(short8_t, u32x4{dspk[4 * t], dspk[4 * t + 1], dspk[4 * t + 2], dspk[4 * t + 3]});
-            const int k0 = wave * 32 + 16 * t + 4 * g;
-#pragma unroll
-            for (int mb = 0; mb < S::MB; ++mb) {
-              const int r0 = k0 + (i16 >> 2), c0 = 16 * (qg & 1) + 32 * mb + 4 * (i16 & 3);
-              short8_t ka = cat4(lds_read_tr(sK, r0 * S::KS + c0), lds_read_tr(sK, (r0 + 8) * S::KS + c0));
-              dq[mb] = T::mfma(ka, db, dq[mb]);
-            }
-          }
-        }
-      }
-    }
-    // ---- sum the 4 waves' dQ^T partials, write dQ = scale * dQ
-    __syncthreads();
-#pragma unroll
-    for (int mb = 0; mb < S::MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sRed[((wave * S::MB + mb) * 16 + r) * 64 + lane] = dq[mb][r];
-    __syncthreads();
-    {
-      // thread t sums element e = t (+256k) of the 16*MB*64 per-wave values
-      constexpr int E = 16 * S::MB * 64;
-      for (int e = tid; e < E; e += 256) {
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < kQWaves; ++w) s += sRed[w * E + e];
-        const int ln = e % 64, r = (e / 64) % 16, mb = e / (64 * 16);
-        const int ii = ib * 32 + (ln & 31);
-        const int d = 32 * mb + 8 * (r / 4) + 4 * (ln >> 5) + (r % 4);
-        if (ii < L && d < D) a.dq[((slice + ii) * H + h) * D + d] = T::from_f32(s * a.scale);
-      }
-    }
-  }
-
-  if constexpr (WANT_DPAIR && DPC > 0) {
-    if (i_valid) {
-      float* dst = a.dpair_part + ((((size_t)ng * a.B + b) * H + h) * L + i) * L;
-#pragma unroll
-      for (int cu = 0; cu < DPC; ++cu) {
-        const int j0 = cu * kQChunk + wave * 32;
-        if (j0 < L) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int jj = j0 + 8 * q + 4 * half;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (jj + u < L) dst[jj + u] = dpacc[cu][4 * q + u];
-          }
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- bwd_fin
 
-// Bias-gradient reductions in one launch.  Threads [0, n_pair) sum the dpair
-// partials of the n-groups (4 consecutive elements each when the element
-// count allows 16-byte access); the rest sum the per-head dmask partials.
-// Both sums run in a fixed order, so the result is bitwise reproducible.
+// Reductions in one launch, each in a fixed order (bitwise reproducible):
+//   threads [0, n_pair)                  dpair = sum of the n-group partials
+//                                        (4 consecutive elements each when
+//                                        the count allows 16-byte access);
+//   [n_pair, n_pair + n_mask)            dmask = sum of the per-head partials;
+//   [n_pair + n_mask, ... + n_dq)        dQ = sum of the key-tile partials
+//                                        (rows longer than one key tile), 4
+//                                        consecutive elements each.
 template <class T, bool VEC>
-__global__ __launch_bounds__(256) void evo_bwd_fin_kernel(BwdArgs a, int ngroups, int from_f32, int64_t n_pair,
-                                                          int64_t n_mask) {
+__global__ __launch_bounds__(256) void evo_bwd_fin_kernel(BwdArgs a, int ngroups, int64_t n_pair, int64_t n_mask,
+                                                          int64_t n_dq, int jtiles) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e < n_pair) {
     const int64_t per = (int64_t)a.B * a.H * a.L * a.L;
     if constexpr (VEC) {
       const int64_t idx = 4 * e;
-      floatx4 s;
-      if (from_f32) {
-        s = *reinterpret_cast<const floatx4*>(a.dpair_f32 + idx);
-      } else {
-        floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
-        int gg = 0;
-        for (; gg + 1 < ngroups; gg += 2) {
-          s0 += *reinterpret_cast<const floatx4*>(a.dpair_part + (int64_t)gg * per + idx);
-          s1 += *reinterpret_cast<const floatx4*>(a.dpair_part + (int64_t)(gg + 1) * per + idx);
-        }
-        if (gg < ngroups) s0 += *reinterpret_cast<const floatx4*>(a.dpair_part + (int64_t)gg * per + idx);
-        s = s0 + s1;
-        *reinterpret_cast<floatx4*>(a.dpair_f32 + idx) = s;
+      floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+      int gg = 0;
+      for (; gg + 1 < ngroups; gg += 2) {
+        s0 += *reinterpret_cast<const floatx4*>(a.dpair_part + (int64_t)gg * per + idx);
+        s1 += *reinterpret_cast<const floatx4*>(a.dpair_part + (int64_t)(gg + 1) * per + idx);
       }
+      if (gg < ngroups) s0 += *reinterpret_cast<const floatx4*>(a.dpair_part + (int64_t)gg * per + idx);
+      const floatx4 s = s0 + s1;
+      *reinterpret_cast<floatx4*>(a.dpair_f32 + idx) = s;
       u32x2 w;
       w[0] = T::pack2(s[0], s[1]);
       w[1] = T::pack2(s[2], s[3]);
       *reinterpret_cast<u32x2*>(a.dpair + idx) = w;
     } else {
-      float s;
-      if (from_f32) {
-        s = a.dpair_f32[e];
-      } else {
-        float s0 = 0.f, s1 = 0.f;
-        int gg = 0;
-        for (; gg + 1 < ngroups; gg += 2) {
-          s0 += a.dpair_part[(int64_t)gg * per + e];
-          s1 += a.dpair_part[(int64_t)(gg + 1) * per + e];
-        }
-        if (gg < ngroups) s0 += a.dpair_part[(int64_t)gg * per + e];
-        s = s0 + s1;
-        a.dpair_f32[e] = s;
+      float s0 = 0.f, s1 = 0.f;
+      int gg = 0;
+      for (; gg + 1 < ngroups; gg += 2) {
+        s0 += a.dpair_part[(int64_t)gg * per + e];
+        s1 += a.dpair_part[(int64_t)(gg + 1) * per + e];
       }
+      if (gg < ngroups) s0 += a.dpair_part[(int64_t)gg * per + e];
+      const float s = s0 + s1;
+      a.dpair_f32[e] = s;
       a.dpair[e] = T::from_f32(s);
     }
     return;
@@ -551,12 +312,18 @@ __global__ __launch_bounds__(256) void evo_bwd_fin_kernel(BwdArgs a, int ngroups
     for (int hh = 0; hh < a.H; ++hh) s += a.dmask_part[(bn * a.H + hh) * a.L + j];
     a.dmask_f32[m] = s;
     a.dmask[m] = T::from_f32(s);
+    return;
   }
-}
-
-__global__ __launch_bounds__(256) void evo_zero_f32_kernel(float* p, int64_t n) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e < n) p[e] = 0.f;
+  const int64_t q = m - n_mask;
+  if (q < n_dq) {
+    const int64_t per = n_dq * 4, idx = 4 * q;
+    floatx4 s = *reinterpret_cast<const floatx4*>(a.dq_part + idx);
+    for (int jt = 1; jt < jtiles; ++jt) s += *reinterpret_cast<const floatx4*>(a.dq_part + (int64_t)jt * per + idx);
+    u32x2 w;
+    w[0] = T::pack2(s[0], s[1]);
+    w[1] = T::pack2(s[2], s[3]);
+    *reinterpret_cast<u32x2*>(a.dq + idx) = w;
+  }
 }
 
 // ------------------------------------------------------------------ launch
@@ -565,62 +332,38 @@ template <class T, int D, bool HM, bool HP>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   const bool want_dmask = a.dmask != nullptr;
   const bool want_dpair = a.dpair != nullptr;
-  const int nchunks = (a.L + kQChunk - 1) / kQChunk;
   const bool fits = a.L <= KVTile<D>::CH;
+  const int jtiles = (a.L + KVTile<D>::CH - 1) / KVTile<D>::CH;
   if (fits) {
     const hipError_t e = launch_bwd_tile(a, D, std::is_same<T, BF16>::value, st);
     if (e != hipSuccess) return e;
   } else {
-    {
-      const int64_t rows = (int64_t)a.B * a.N * a.L * a.H;
-      prof_begin(K_BWD_PRE, st);
-      hipLaunchKernelGGL((evo_bwd_pre_kernel<T, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a);
-      prof_end(K_BWD_PRE, st);
-    }
-    {
-      const int grid = a.B * a.N * a.H * ((a.L + kKvKeys - 1) / kKvKeys);
-      prof_begin(K_BWD_KV, st);
-      if (want_dmask)
-        hipLaunchKernelGGL((evo_bwd_kv_kernel<T, D, HM, HP, true>), dim3(grid), dim3(256), 0, st, a);
-      else
-        hipLaunchKernelGGL((evo_bwd_kv_kernel<T, D, HM, HP, false>), dim3(grid), dim3(256), 0, st, a);
-      prof_end(K_BWD_KV, st);
-    }
-    {
-      const int grid = a.B * a.H * ((a.L + 31) / 32) * a.n_groups_q;
-      if (want_dpair && nchunks > 6) {
-        const int64_t n = (int64_t)a.B * a.H * a.L * a.L;
-        hipLaunchKernelGGL(evo_zero_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.dpair_f32, n);
-      }
-      prof_begin(K_BWD_Q, st);
-      if (!want_dpair) {
-        hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, false, 0>), dim3(grid), dim3(256), 0, st, a);
-      } else if (nchunks <= 2) {
-        hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, true, 2>), dim3(grid), dim3(256), 0, st, a);
-      } else if (nchunks <= 4) {
-        hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, true, 4>), dim3(grid), dim3(256), 0, st, a);
-      } else if (nchunks <= 6) {
-        hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, true, 6>), dim3(grid), dim3(256), 0, st, a);
-      } else {
-        hipLaunchKernelGGL((evo_bwd_q_kernel<T, D, HM, HP, true, 0>), dim3(grid), dim3(256), 0, st, a);
-      }
-      prof_end(K_BWD_Q, st);
-    }
+    // bwd_q3 over key tiles (dQ partials, delta, dpair partials), then the
+    // key-side kernel, which reads delta
+    hipError_t e = launch_bwd_q_split(a, D, std::is_same<T, BF16>::value, st);
+    if (e != hipSuccess) return e;
+    const int grid = a.B * a.N * a.H * ((a.L + kKvKeys - 1) / kKvKeys);
+    prof_begin(K_BWD_KV, st);
+    if (want_dmask)
+      hipLaunchKernelGGL((evo_bwd_kv_kernel<T, D, HM, HP, true>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((evo_bwd_kv_kernel<T, D, HM, HP, false>), dim3(grid), dim3(256), 0, st, a);
+    prof_end(K_BWD_KV, st);
   }
-  if (want_dmask || want_dpair) {
-    const int64_t per = (int64_t)a.B * a.H * a.L * a.L;
-    const bool vec = (per % 4) == 0;
-    const int64_t n_pair = want_dpair ? (vec ? per / 4 : per) : 0;
-    const int64_t n_mask = want_dmask ? (int64_t)a.B * a.N * a.L : 0;
-    const int from_f32 = (!fits && nchunks > 6) ? 1 : 0;
-    const unsigned blocks = (unsigned)((n_pair + n_mask + 255) / 256);
+  const int64_t per = (int64_t)a.B * a.H * a.L * a.L;
+  const bool vec = (per % 4) == 0;
+  const int64_t n_pair = want_dpair ? (vec ? per / 4 : per) : 0;
+  const int64_t n_mask = want_dmask ? (int64_t)a.B * a.N * a.L : 0;
+  const int64_t n_dq = fits ? 0 : (int64_t)a.B * a.N * a.L * a.H * D / 4;
+  if (n_pair + n_mask + n_dq > 0) {
+    const unsigned blocks = (unsigned)((n_pair + n_mask + n_dq + 255) / 256);
     prof_begin(K_BWD_FIN, st);
     if (vec)
-      hipLaunchKernelGGL((evo_bwd_fin_kernel<T, true>), dim3(blocks), dim3(256), 0, st, a, a.n_groups_q, from_f32,
-                         n_pair, n_mask);
+      hipLaunchKernelGGL((evo_bwd_fin_kernel<T, true>), dim3(blocks), dim3(256), 0, st, a, a.n_groups_q, n_pair,
+                         n_mask, n_dq, jtiles);
     else
-      hipLaunchKernelGGL((evo_bwd_fin_kernel<T, false>), dim3(blocks), dim3(256), 0, st, a, a.n_groups_q, from_f32,
-                         n_pair, n_mask);
+      hipLaunchKernelGGL((evo_bwd_fin_kernel<T, false>), dim3(blocks), dim3(256), 0, st, a, a.n_groups_q, n_pair,
+                         n_mask, n_dq, jtiles);
     prof_end(K_BWD_FIN, st);
   }
   return hipGetLastError();

@@ -36,8 +36,8 @@ namespace evo {
 constexpr int kWaves = 8;
 
 // Per-thread byte offsets, relative to the first element of a (b, n) slice,
-// of the 16-byte chunks this thread copies into a tile (rows = keys [0, CH),
-// clamped to L - 1; K-layout chunks first, then V-layout chunks).  They do not
+// of the 16-byte chunks this thread copies into a tile (rows = keys
+// [kc0, kc0 + CH), clamped to L - 1; K-layout chunks first, then V-layout chunks).  They do not
 // depend on n, so the per-slice copy is a base pointer plus these offsets.
 template <int D, int NT>
 struct TileCopy {
@@ -46,7 +46,8 @@ struct TileCopy {
 };
 
 template <int D, int NT>
-__device__ __forceinline__ void tile_chunk_offsets(TileCopy<D, NT>& tc, int L, int H, int h, int wave, int lane) {
+__device__ __forceinline__ void tile_chunk_offsets(TileCopy<D, NT>& tc, int kc0, int L, int H, int h, int wave,
+                                                   int lane) {
   using TL = KVTile<D>;
 #pragma unroll
   for (int c = 0; c < TileCopy<D, NT>::N; ++c) {
@@ -61,7 +62,7 @@ __device__ __forceinline__ void tile_chunk_offsets(TileCopy<D, NT>& tc, int L, i
       cc = (q2 % TL::VC) ^ kv_swz<TL::VC>(r);
       if (cc >= D / 8) cc = 0;  // columns the transposed reads touch but never use
     }
-    const int j = min(r, L - 1);
+    const int j = min(kc0 + r, L - 1);
     tc.off[c] = (uint32_t)((((size_t)j * H + h) * D + 8 * cc) * 2);
   }
 }
@@ -92,7 +93,7 @@ __device__ __forceinline__ void issue_tile(uint8_t* buf, const uint16_t* kx, con
 //   P = exp2((S*scale + pair) log2e - lse log2e),  dS^T = P dP^T
 //   dQ^T += K^T dS^T                     (K^T by transposed LDS reads)
 //   dpair^T[block] += I dS^T[block]      (16x16x16 MFMA against an identity)
-template <class T, int D, bool HAS_PAIR, bool WANT_DPAIR, int NW>
+template <class T, int D, bool HAS_PAIR, bool WANT_DPAIR, bool SPLIT, int NW>
 __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   using TL = KVTile<D>;
   constexpr int KS32 = (D + 31) / 32;  // 32-wide k-steps over d
@@ -113,6 +114,13 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   int rest = wg / H;
   const int it = rest % itiles;
   rest /= itiles;
+  // rows longer than one key tile: each workgroup takes one key tile and
+  // leaves an fp32 partial of dQ, summed over the tiles by bwd_fin
+  const int jtiles = SPLIT ? (L + TL::CH - 1) / TL::CH : 1;
+  const int jt = SPLIT ? rest % jtiles : 0;
+  if constexpr (SPLIT) rest /= jtiles;
+  const int kc0 = jt * TL::CH;
+  const int lk = L - kc0;  // keys of the row from this tile on
   const int ng = rest % a.n_groups_q;
   const int b = rest / a.n_groups_q;
   const int i = it * kRows + wave * 16 + col;
@@ -122,14 +130,14 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   const int ntiles = n_end - n_begin;
   const float scale = a.scale, c1 = a.scale * kLog2e;
 
-  // resident pair bias: block blk, lane gets pair[ic][16 blk + 4 g + 0..3]
+  // resident pair bias: block blk, lane gets pair[ic][kc0 + 16 blk + 4 g + 0..3]
   u32x2 pbias[HAS_PAIR ? NB : 1];
   if constexpr (HAS_PAIR) {
     const uint16_t* prow = a.pair + (((size_t)b * H + h) * L + ic) * L;
     const bool pvec = (L % 4) == 0;
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
-      const int j = 16 * blk + 4 * g;
+      const int j = kc0 + 16 * blk + 4 * g;
       u32x2 v;
       if (pvec) {
         v = *reinterpret_cast<const u32x2*>(prow + min(j, L - 4));
@@ -149,7 +157,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   for (int e = 0; e < 4; ++e) ident[e] = (4 * g + e == col) ? T::one() : (short)0;
 
   TileCopy<D, NT> coff;
-  tile_chunk_offsets<D, NT>(coff, L, H, h, wave, lane);
+  tile_chunk_offsets<D, NT>(coff, kc0, L, H, h, wave, lane);
 
   short8_t qop[KS32], gop[KS32], qnx[KS32], gnx[KS32], onx[KS32];
   float lse_nx = 0.f;
@@ -171,10 +179,10 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
       onx[s] = ov;
     }
     lse_nx = a.lse[(((size_t)b * N + n) * H + h) * L + ic];
-    if (mask_thread) mraw = a.mask ? a.mask[((size_t)b * N + n) * L + min(tid, L - 1)] : 0u;
+    if (mask_thread) mraw = a.mask ? a.mask[((size_t)b * N + n) * L + min(kc0 + tid, L - 1)] : 0u;
   };
   auto store_mask = [&](int buf) {
-    if (mask_thread) smk[buf][tid] = (tid < L) ? T::to_f32((uint16_t)mraw) * a.sqrt_d : kNegInf;
+    if (mask_thread) smk[buf][tid] = (tid < lk) ? T::to_f32((uint16_t)mraw) * a.sqrt_d : kNegInf;
   };
   auto slice_ptr = [&](const uint16_t* base, int n) { return base + ((size_t)b * N + n) * L * H * D; };
 
@@ -182,17 +190,17 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
 #pragma unroll
   for (int blk = 0; blk < (WANT_DPAIR ? NB : 1); ++blk) dpacc[blk] = floatx4{0.f, 0.f, 0.f, 0.f};
   // the group's fp32 dpair partial of block blk (keys 16 blk + 4 g + 0..3 of query i)
-  float* const dpdst = WANT_DPAIR ? a.dpair_part + ((((size_t)ng * a.B + b) * H + h) * L + ic) * L : nullptr;
+  float* const dpdst = WANT_DPAIR ? a.dpair_part + ((((size_t)ng * a.B + b) * H + h) * L + ic) * L + kc0 : nullptr;
   auto store_dpair = [&](int blk) {
     if constexpr (WANT_DPAIR) {
       if (!i_valid) return;
       const int j = 16 * blk + 4 * g;
-      if (j + 4 <= L && (L % 4) == 0) {
+      if (j + 4 <= lk && (L % 4) == 0) {
         *reinterpret_cast<floatx4*>(dpdst + j) = dpacc[blk];
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (j + u < L) dpdst[j + u] = dpacc[blk][u];
+          if (j + u < lk) dpdst[j + u] = dpacc[blk][u];
       }
     }
   };
@@ -226,7 +234,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
       part += __shfl_xor(part, 16);
       part += __shfl_xor(part, 32);
       del = part;
-      if (g == 0 && i_valid) a.delta[(((size_t)b * N + n) * H + h) * L + i] = del;
+      if (g == 0 && i_valid && jt == 0) a.delta[(((size_t)b * N + n) * H + h) * L + i] = del;
     }
     const floatx4 ndel = {-del, -del, -del, -del};
     if (t + 1 < ntiles) {
@@ -330,7 +338,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
           store_dpair(2 * st - 1);
         }
       }
-      if (32 * st < L) {
+      if (32 * st < lk) {
         short4_t kt[2 * MB];  // [mb][lo/hi 16 keys]
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -372,15 +380,20 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     });
     // ---- dQ = scale * dQ^T: lane holds d = 16 mb + 4 g + 0..3 of query i
     if (i_valid) {
-      uint16_t* dqrow = a.dq + ((((size_t)b * N + n) * L + i) * H + h) * D;
+      const size_t row = (((size_t)b * N + n) * L + i) * H + h;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int d = 16 * mb + 4 * g;
         if (d < D) {
-          u32x2 w;
-          w[0] = T::pack2(dq[mb][0] * scale, dq[mb][1] * scale);
-          w[1] = T::pack2(dq[mb][2] * scale, dq[mb][3] * scale);
-          *reinterpret_cast<u32x2*>(dqrow + d) = w;
+          if constexpr (SPLIT) {
+            float* dst = a.dq_part + ((size_t)jt * a.B * N * L * H + row) * D + d;
+            *reinterpret_cast<floatx4*>(dst) = dq[mb] * scale;
+          } else {
+            u32x2 w;
+            w[0] = T::pack2(dq[mb][0] * scale, dq[mb][1] * scale);
+            w[1] = T::pack2(dq[mb][2] * scale, dq[mb][3] * scale);
+            *reinterpret_cast<u32x2*>(a.dq + row * D + d) = w;
+          }
         }
       }
     }
@@ -490,7 +503,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   }
 
   TileCopy<D, NT> coff;
-  tile_chunk_offsets<D, NT>(coff, L, H, h, wave, lane);
+  tile_chunk_offsets<D, NT>(coff, 0, L, H, h, wave, lane);
 
   // ---- per-slice key operands (B of S = Q K^T and dP = dO V^T): lane = key
   short8_t kop[KS32], vop[KS32], knx[KS32], vnx[KS32];
@@ -720,9 +733,9 @@ static hipError_t launch_tile_t(const BwdArgs& a, hipStream_t st) {
   const int gridq = a.B * a.H * ((a.L + kRows - 1) / kRows) * a.n_groups_q;
   prof_begin(K_BWD_Q, st);
   if (want_dpair)
-    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, true, NW>), dim3(gridq), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, true, false, NW>), dim3(gridq), dim3(64 * NW), 0, st, a);
   else
-    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, false, NW>), dim3(gridq), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, false, false, NW>), dim3(gridq), dim3(64 * NW), 0, st, a);
   prof_end(K_BWD_Q, st);
   const int gridk = a.B * a.H * ((a.L + kRows - 1) / kRows) * ((a.N + a.Gq - 1) / a.Gq);
   prof_begin(K_BWD_KV, st);
@@ -752,6 +765,36 @@ static hipError_t launch_tile_dt(const BwdArgs& a, int D, hipStream_t st) {
 
 hipError_t launch_bwd_tile(const BwdArgs& a, int D, bool bf16, hipStream_t stream) {
   return bf16 ? launch_tile_dt<BF16>(a, D, stream) : launch_tile_dt<F16>(a, D, stream);
+}
+
+template <class T, int D, bool HP>
+static hipError_t launch_split_t(const BwdArgs& a, hipStream_t st) {
+  constexpr int NW = kWaves, kRows = 16 * kWaves;
+  const int jtiles = (a.L + KVTile<D>::CH - 1) / KVTile<D>::CH;
+  const int grid = a.B * a.H * ((a.L + kRows - 1) / kRows) * jtiles * a.n_groups_q;
+  prof_begin(K_BWD_Q, st);
+  if (a.dpair)
+    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, true, true, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
+  else
+    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, false, true, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
+  prof_end(K_BWD_Q, st);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_split_dt(const BwdArgs& a, int D, hipStream_t st) {
+  const bool hp = a.pair != nullptr;
+  switch (D) {
+    case 8: return hp ? launch_split_t<T, 8, true>(a, st) : launch_split_t<T, 8, false>(a, st);
+    case 16: return hp ? launch_split_t<T, 16, true>(a, st) : launch_split_t<T, 16, false>(a, st);
+    case 32: return hp ? launch_split_t<T, 32, true>(a, st) : launch_split_t<T, 32, false>(a, st);
+    case 64: return hp ? launch_split_t<T, 64, true>(a, st) : launch_split_t<T, 64, false>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_q_split(const BwdArgs& a, int D, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_split_dt<BF16>(a, D, stream) : launch_split_dt<F16>(a, D, stream);
 }
 
 }  // namespace evo

@@ -41,6 +41,7 @@ struct BwdArgs {
   float* dmask_f32;      // [B,N,L]
   float* dpair_part;     // [n_groups_q, B, H, L, L] (when dpair requested)
   float* dpair_f32;      // [B,H,L,L]
+  float* dq_part;        // [jtiles, B,N,L,H,D] fp32 partials of dQ (rows longer than one key tile)
   int B, N, L, H;
   int Gq;          // slices per bwd_q workgroup
   int n_groups_q;
@@ -66,5 +67,7 @@ hipError_t launch_fwd(FwdArgs a, int D, bool bf16, hipStream_t stream);
 hipError_t launch_bwd(BwdArgs a, int D, bool bf16, hipStream_t stream);
 // backward for rows that fit one key tile (L <= 256, or 128 at D = 64): bwd_q3 then bwd_kv3
 hipError_t launch_bwd_tile(const BwdArgs& a, int D, bool bf16, hipStream_t stream);
+// bwd_q3 for longer rows: one key tile per workgroup, dQ left as fp32 partials
+hipError_t launch_bwd_q_split(const BwdArgs& a, int D, bool bf16, hipStream_t stream);
 
 }  // namespace evo
