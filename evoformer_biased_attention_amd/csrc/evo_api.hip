@@ -183,6 +183,19 @@ int plan_bwdq_group(const Shape& s) {
   return env_int("EVOATTN_BWD_GQ", (int)g);
 }
 
+// slices per bwd_kv3 workgroup: same rule over the key-side grid (one
+// workgroup per 128 keys and slice group)
+int plan_bwdkv_group(const Shape& s) {
+  const int64_t per_group = s.B * s.H * ((s.L + 127) / 128);
+  const int64_t kmax = s.N < 4096 ? s.N : 4096;
+  auto cost = [&](int64_t k) { return ((per_group * k + 255) / 256) * ((s.N + k - 1) / k); };
+  int64_t best_t = INT64_MAX;
+  for (int64_t k = 1; k <= kmax; ++k) best_t = std::min(best_t, cost(k));
+  int64_t k = 1;
+  while (k < kmax && cost(k) * 100 > best_t * 103) ++k;
+  return (int)((s.N + k - 1) / k);
+}
+
 struct WsLayout {
   size_t delta, dmask_part, dmask_f32, dpair_part, dpair_f32, dq_part, total;
   int gq, ngq;
@@ -414,6 +427,8 @@ evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const voi
   a.H = (int)s.H;
   a.Gq = w.gq;
   a.n_groups_q = w.ngq;
+  a.Gk = plan_bwdkv_group(s);
+  a.n_groups_k = (int)((s.N + a.Gk - 1) / a.Gk);
   a.sqrt_d = (float)std::sqrt((double)s.D);
   a.scale = (float)(1.0 / std::sqrt((double)s.D));
   sqrt_split(s.D, dtype == EVO_BF16, &a.s_hi, &a.s_lo);

@@ -420,9 +420,13 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
 //   P = exp2(...),  dS = P dP
 //   dV^T += dO^T P,  dK^T += Q^T dS      (dO^T, Q^T by transposed LDS reads)
 //   dmask partial += column sums of dS   (MFMA against a row of ones)
-// The pair-bias columns of the workgroup's keys are read once per workgroup (through
-// LDS, transposed) and stay in registers for the whole n-group.
-template <class T, int D, bool HAS_PAIR, bool WANT_DMASK, int NW>
+// Rows that fit one query tile: the pair-bias columns of the workgroup's keys
+// are read once per workgroup (through LDS, transposed) and stay in registers
+// for the whole n-group.  Longer rows (MULTI): per n the queries come in
+// tiles of CH; dK, dV and dmask accumulate over the tiles, and the bias
+// columns of each (n, tile) are staged through a slab of their own while the
+// previous tile is computed.
+template <class T, int D, bool HAS_PAIR, bool WANT_DMASK, bool MULTI, int NW>
 __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   using TL = KVTile<D>;
   constexpr int KS32 = (D + 31) / 32;
@@ -431,9 +435,10 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   constexpr int MB = (D + 15) / 16;
   constexpr int KC = TL::KC, VC = TL::VC;
   constexpr int NT = 64 * NW, kRows = 16 * NW;
-  constexpr int kSlab = HAS_PAIR ? TL::CH * kRows * 2 : 0;  // pair[:, the workgroup's keys] staged once
-  constexpr int kSmem = 2 * TL::BUF_BYTES > kSlab ? 2 * TL::BUF_BYTES : kSlab;
+  constexpr int kSlab = HAS_PAIR ? TL::CH * kRows * 2 : 0;  // pair[CH queries][the workgroup's keys]
+  constexpr int kSmem = (MULTI || 2 * TL::BUF_BYTES > kSlab) ? 2 * TL::BUF_BYTES : kSlab;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+  __shared__ __attribute__((aligned(16))) uint8_t sslab[(MULTI && HAS_PAIR) ? kSlab : 16];
   __shared__ __attribute__((aligned(16))) float slse[2][TL::CH];  // -lse log2e; -inf past L / no finite score
   __shared__ __attribute__((aligned(16))) float sndel[2][TL::CH]; // -delta
 
@@ -441,7 +446,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   const int g = lane >> 4, col = lane & 15;
   const int L = a.L, H = a.H, N = a.N;
   const int jtiles = (L + kRows - 1) / kRows;
-  const int ngroups = (N + a.Gq - 1) / a.Gq;
+  const int ngroups = a.n_groups_k;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int h = wg % H;
   int rest = wg / H;
@@ -452,46 +457,58 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   const int j = jt * kRows + wave * 16 + col;  // this lane's key
   const bool j_valid = j < L;
   const int jc = min(j, L - 1);
-  const int n_begin = ng * a.Gq, n_end = min(N, n_begin + a.Gq);
+  const int n_begin = ng * a.Gk, n_end = min(N, n_begin + a.Gk);
   const int ntiles = n_end - n_begin;
+  const int qtiles = MULTI ? (L + TL::CH - 1) / TL::CH : 1;  // query tiles per slice
+  const int nu = ntiles * qtiles;                             // (n, query tile) steps
   const float scale = a.scale, c1 = a.scale * kLog2e;
+  const uint16_t* pbase = HAS_PAIR ? a.pair + ((size_t)b * H + h) * L * L : nullptr;
+  const int kc0k = jt * kRows;  // the workgroup's first key
 
-  // ---- pair bias, resident: block qb, lane gets pair[16 qb + 4 g + r][j], r = 0..3
+  // pair[q0 + 0..CH)[the workgroup's keys] row-major (2 kRows-byte rows) into
+  // an LDS slab by 16-byte copies (L % 8 == 0)
+  auto issue_slab = [&](uint8_t* dst, int q0) {
+    constexpr int RC = kRows / 8;  // 16-byte chunks per slab row
+    for (int base = wave * 64; base < TL::CH * RC; base += NT) {
+      const int q = base + lane;
+      const int r = q / RC, c = q % RC;
+      const uint16_t* src = pbase + (size_t)min(q0 + r, L - 1) * L + min(kc0k + 8 * c, L - 8);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(dst + base * 16), 16, 0, 0);
+    }
+  };
+  // bias block qb of a query tile: lane gets pair[q0 + 16 qb + 4 g + r][j], r = 0..3
   u32x2 pbias[HAS_PAIR ? NB : 1];
-  if constexpr (HAS_PAIR) {
-    const uint16_t* pbase = a.pair + ((size_t)b * H + h) * L * L;
+  auto read_slab = [&](const uint8_t* src) {
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      const int row = 16 * qb + 4 * g + (col >> 2);
+      const int kcol = wave * 16 + 4 * (col & 3);
+      pbias[qb] = __builtin_bit_cast(u32x2, lds_read_tr_b(src, (row * kRows + kcol) * 2));
+    }
+  };
+  auto gather_bias = [&](int q0) {  // L % 8 != 0: column reads straight from memory
+    const uint16_t* prow = pbase + jc;
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      uint32_t t4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t4[r] = prow[(size_t)min(q0 + 16 * qb + 4 * g + r, L - 1) * L];
+      pbias[qb][0] = t4[0] | (t4[1] << 16);
+      pbias[qb][1] = t4[2] | (t4[3] << 16);
+    }
+  };
+
+  // ---- resident pair bias (one query tile)
+  if constexpr (HAS_PAIR && !MULTI) {
     if ((L % 8) == 0) {
-      // stage pair[0..L)[the workgroup's keys] row-major (2 kRows-byte rows)
-      // with 16-byte copies, then read columns with transposed reads
-      constexpr int RC = kRows / 8;  // 16-byte chunks per slab row
-      const int kc0 = jt * kRows;
-      for (int base = wave * 64; base < TL::CH * RC; base += NT) {
-        const int q = base + lane;
-        const int r = q / RC, c = q % RC;
-        const uint16_t* src = pbase + (size_t)min(r, L - 1) * L + min(kc0 + 8 * c, L - 8);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)(smem + base * 16), 16, 0, 0);
-      }
+      issue_slab(smem, 0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        const int row = 16 * qb + 4 * g + (col >> 2);
-        const int kcol = wave * 16 + 4 * (col & 3);
-        const short4_t v = lds_read_tr_b(smem, (row * kRows + kcol) * 2);
-        pbias[qb] = __builtin_bit_cast(u32x2, v);
-      }
+      read_slab(smem);
       __syncthreads();
     } else {
-      const uint16_t* prow = pbase + jc;
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        uint32_t t4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) t4[r] = prow[(size_t)min(16 * qb + 4 * g + r, L - 1) * L];
-        pbias[qb][0] = t4[0] | (t4[1] << 16);
-        pbias[qb][1] = t4[2] | (t4[3] << 16);
-      }
+      gather_bias(0);
     }
   }
 
@@ -510,7 +527,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   uint32_t mnx = 0;
   float lse_nx = 0.f, del_nx = 0.f;
   const bool row_thread = tid < TL::CH;
-  auto load_keys = [&](int n) {
+  auto load_keys = [&](int n) {  // K, V rows and the mask of the lane's key
     const size_t row = (((size_t)b * N + n) * L + jc) * H + h;
 #pragma unroll
     for (int s = 0; s < KS32; ++s) {
@@ -524,8 +541,13 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
       vnx[s] = vv;
     }
     mnx = a.mask ? a.mask[((size_t)b * N + n) * L + jc] : 0u;
+  };
+  auto slice_ptr = [&](const uint16_t* base, int n) { return base + ((size_t)b * N + n) * L * H * D; };
+  int q0_nx = 0;
+  auto load_rows = [&](int n, int q0) {  // lse, delta of query q0 + tid
+    q0_nx = q0;
     if (row_thread) {
-      const size_t ri = (((size_t)b * N + n) * H + h) * L + min(tid, L - 1);
+      const size_t ri = (((size_t)b * N + n) * H + h) * L + min(q0 + tid, L - 1);
       lse_nx = a.lse[ri];
       del_nx = a.delta[ri];
     }
@@ -533,35 +555,77 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   auto store_rows = [&](int buf) {
     if (row_thread) {
       // queries past L, or with no finite score, get P = 0
-      slse[buf][tid] = (tid < L && lse_nx != kNegInf) ? -lse_nx * kLog2e : kNegInf;
+      slse[buf][tid] = (q0_nx + tid < L && lse_nx != kNegInf) ? -lse_nx * kLog2e : kNegInf;
       sndel[buf][tid] = -del_nx;
     }
   };
-  auto slice_ptr = [&](const uint16_t* base, int n) { return base + ((size_t)b * N + n) * L * H * D; };
+  // the asynchronous copy of step u's Q and dO tile into buffer buf
+  auto issue_qo = [&](int u, int buf) {
+    const int n = n_begin + u / qtiles, q0 = (u % qtiles) * TL::CH;
+    const uint16_t* qs = slice_ptr(a.q, n);
+    const uint16_t* os = slice_ptr(a.dout, n);
+    uint8_t* dst = smem + buf * TL::BUF_BYTES;
+    if constexpr (MULTI) {
+      TileCopy<D, NT> tc;
+      tile_chunk_offsets<D, NT>(tc, q0, L, H, h, wave, lane);
+      issue_tile<D, NT>(dst, qs, os, tc, wave);
+    } else {
+      issue_tile<D, NT>(dst, qs, os, coff, wave);
+    }
+  };
 
-  if (ntiles > 0) {
+  floatx4 mk4 = {0.f, 0.f, 0.f, 0.f};
+  floatx4 dk[MB], dv[MB], dmk = {0.f, 0.f, 0.f, 0.f};
+  if (nu > 0) {
     load_keys(n_begin);
-    issue_tile<D, NT>(smem, slice_ptr(a.q, n_begin), slice_ptr(a.dout, n_begin), coff, wave);
+    load_rows(n_begin, 0);
+    issue_qo(0, 0);
+    if constexpr (MULTI && HAS_PAIR) {
+      if ((L % 8) == 0) issue_slab(sslab, 0);
+    }
     store_rows(0);
   }
-  for (int t = 0; t < ntiles; ++t) {
+  for (int u = 0; u < nu; ++u) {
+    const int t = u / qtiles, qt = u % qtiles, q0 = qt * TL::CH;
     const int n = n_begin + t;
+    const int lq = L - q0;  // queries of the row from this tile on
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (qt == 0) {
 #pragma unroll
-    for (int s = 0; s < KS32; ++s) {
-      kop[s] = knx[s];
-      vop[s] = vnx[s];
+      for (int s = 0; s < KS32; ++s) {
+        kop[s] = knx[s];
+        vop[s] = vnx[s];
+      }
+      // sqrt(D) * mask of the lane's key as the score accumulator input
+      const float mk = j_valid ? T::to_f32((uint16_t)mnx) * a.sqrt_d : kNegInf;
+      mk4 = floatx4{mk, mk, mk, mk};
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        dk[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        dv[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+      dmk = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    // sqrt(D) * mask of the lane's key as the score accumulator input
-    const float mk = j_valid ? T::to_f32((uint16_t)mnx) * a.sqrt_d : kNegInf;
-    const floatx4 mk4 = {mk, mk, mk, mk};
-    if (t + 1 < ntiles) {
-      issue_tile<D, NT>(smem + ((t + 1) & 1) * TL::BUF_BYTES, slice_ptr(a.q, n + 1), slice_ptr(a.dout, n + 1), coff,
-                        wave);
-      load_keys(n + 1);
+    if constexpr (MULTI && HAS_PAIR) {
+      // this tile's bias columns; the slab is then free for the next tile's
+      if ((L % 8) == 0) {
+        read_slab(sslab);
+        __syncthreads();
+      } else {
+        gather_bias(q0);
+      }
     }
-    const uint8_t* qb_ = smem + (t & 1) * TL::BUF_BYTES;
+    if (u + 1 < nu) {
+      const int n1 = n_begin + (u + 1) / qtiles, qt1 = (u + 1) % qtiles;
+      issue_qo(u + 1, (u + 1) & 1);
+      if constexpr (MULTI && HAS_PAIR) {
+        if ((L % 8) == 0) issue_slab(sslab, qt1 * TL::CH);
+      }
+      load_rows(n1, qt1 * TL::CH);
+      if (qt1 == 0) load_keys(n1);
+    }
+    const uint8_t* qb_ = smem + (u & 1) * TL::BUF_BYTES;
     const uint8_t* ob_ = qb_ + TL::KCH * 16;
     // per-lane LDS byte addresses (see bwd_q3)
     uint32_t qaddr[KS32], oaddr[KS32];
@@ -571,7 +635,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
       qaddr[s] = lds_addr(qb_ + (col * KC + ((c < KC ? c : 0) ^ kv_swz<KC>(col))) * 16);
       oaddr[s] = lds_addr(ob_ + (col * VC + ((c < VC ? c : 0) ^ kv_swz<VC>(col))) * 16);
     }
-    const uint32_t laddr = lds_addr(&slse[t & 1][4 * g]), daddr = lds_addr(&sndel[t & 1][4 * g]);
+    const uint32_t laddr = lds_addr(&slse[u & 1][4 * g]), daddr = lds_addr(&sndel[u & 1][4 * g]);
     uint32_t qtaddr[MB], otaddr[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -630,12 +694,6 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
       }
     };
 
-    floatx4 dk[MB], dv[MB], dmk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      dk[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      dv[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
     floatx4 sc[2][2], dp[2][2];
     StepOps ops;
     load_ops(std::integral_constant<int, 0>{}, ops);
@@ -652,7 +710,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
         products(ops, sc[cur ^ 1], dp[cur ^ 1]);
         if constexpr (st + 2 < NSTEP) load_ops(std::integral_constant<int, st + 2>{}, ops);
       }
-      if (32 * st < L) {
+      if (32 * st < lq) {
         short4_t tt[4 * MB];  // [mb][q lo, q hi, o lo, o hi]
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -701,7 +759,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
       }
     });
     // ---- dK = scale * dK^T, dV: lane holds d = 16 mb + 4 g + 0..3 of key j
-    if (j_valid) {
+    if (j_valid && qt == qtiles - 1) {
       const size_t row = (((size_t)b * N + n) * L + j) * H + h;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -718,7 +776,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
       }
       if (WANT_DMASK && g == 0) a.dmask_part[(((size_t)b * N + n) * H + h) * L + j] = dmk[0];
     }
-    if (t + 1 < ntiles) store_rows((t + 1) & 1);
+    if (u + 1 < nu) store_rows((u + 1) & 1);
   }
 }
 
@@ -737,12 +795,12 @@ static hipError_t launch_tile_t(const BwdArgs& a, hipStream_t st) {
   else
     hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, false, false, NW>), dim3(gridq), dim3(64 * NW), 0, st, a);
   prof_end(K_BWD_Q, st);
-  const int gridk = a.B * a.H * ((a.L + kRows - 1) / kRows) * ((a.N + a.Gq - 1) / a.Gq);
+  const int gridk = a.B * a.H * ((a.L + kRows - 1) / kRows) * a.n_groups_k;
   prof_begin(K_BWD_KV, st);
   if (want_dmask)
-    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, true, NW>), dim3(gridk), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, true, false, NW>), dim3(gridk), dim3(64 * NW), 0, st, a);
   else
-    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, false, NW>), dim3(gridk), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, false, false, NW>), dim3(gridk), dim3(64 * NW), 0, st, a);
   prof_end(K_BWD_KV, st);
   return hipGetLastError();
 }
@@ -778,6 +836,14 @@ static hipError_t launch_split_t(const BwdArgs& a, hipStream_t st) {
   else
     hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, false, true, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
   prof_end(K_BWD_Q, st);
+  // key side over query tiles; it reads the delta bwd_q3 wrote
+  const int gridk = a.B * a.H * ((a.L + kRows - 1) / kRows) * a.n_groups_k;
+  prof_begin(K_BWD_KV, st);
+  if (a.dmask)
+    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, true, true, NW>), dim3(gridk), dim3(64 * NW), 0, st, a);
+  else
+    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, false, true, NW>), dim3(gridk), dim3(64 * NW), 0, st, a);
+  prof_end(K_BWD_KV, st);
   return hipGetLastError();
 }
 

@@ -43,8 +43,10 @@ struct BwdArgs {
   float* dpair_f32;      // [B,H,L,L]
   float* dq_part;        // [jtiles, B,N,L,H,D] fp32 partials of dQ (rows longer than one key tile)
   int B, N, L, H;
-  int Gq;          // slices per bwd_q workgroup
+  int Gq;          // slices per bwd_q3 workgroup
   int n_groups_q;
+  int Gk;          // slices per bwd_kv3 workgroup
+  int n_groups_k;
   float scale;
   float sqrt_d;    // sqrt(D) in fp32 (the masks enter the score accumulators pre-multiplied by it)
   uint16_t s_hi, s_lo;
@@ -67,7 +69,8 @@ hipError_t launch_fwd(FwdArgs a, int D, bool bf16, hipStream_t stream);
 hipError_t launch_bwd(BwdArgs a, int D, bool bf16, hipStream_t stream);
 // backward for rows that fit one key tile (L <= 256, or 128 at D = 64): bwd_q3 then bwd_kv3
 hipError_t launch_bwd_tile(const BwdArgs& a, int D, bool bf16, hipStream_t stream);
-// bwd_q3 for longer rows: one key tile per workgroup, dQ left as fp32 partials
+// longer rows: bwd_q3 with one key tile per workgroup (dQ left as fp32
+// partials), then bwd_kv3 over query tiles
 hipError_t launch_bwd_q_split(const BwdArgs& a, int D, bool bf16, hipStream_t stream);
 
 }  // namespace evo
