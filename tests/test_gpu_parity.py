@@ -91,6 +91,11 @@ SMALL = [
     I.custom("l800_atomic_dpair_bf16", 1, 2, 800, 1, 32, "bf16", 0.05, 1.0, 21),
     I.custom("n_odd_groups", 1, 37, 64, 2, 32, "bf16", 0.1, 1.0, 22),
     I.custom("pair_big_sigma", 1, 4, 96, 2, 32, "fp16", 0.1, 4.0, 23),
+    # rows longer than one key tile: split query side, tiled key side
+    I.custom("l600_no_bias", 1, 2, 600, 2, 32, "fp16", None, None, 24),
+    I.custom("l384_mask_only_bf16", 1, 3, 384, 2, 16, "bf16", 0.1, None, 25),
+    I.custom("l260_d64_gathered_bias", 1, 2, 260, 2, 64, "fp16", 0.1, 1.0, 26),
+    I.custom("l513_d8_bf16", 1, 2, 513, 1, 8, "bf16", 0.05, 1.0, 27),
 ]
 
 
@@ -100,6 +105,29 @@ def test_parity_small_shapes(cfg):
     bits = I.make_inputs(cfg)
     res = _run_gpu(cfg, bits)
     _compare(cfg, bits, res)
+
+
+@pytest.mark.parametrize("cfg", [SMALL[3], SMALL[-2]], ids=["l200_d64", "l260_d64"])
+def test_parity_without_bias_gradients(cfg):
+    """Only dQ, dK, dV requested: the kernels that skip the bias-gradient work."""
+    from evoformer_biased_attention_amd.attention import attn_bwd, attn_fwd
+
+    print(f"case no-bias-grads {cfg.name} shape={cfg.shape} dtype={cfg.dtype}", flush=True)
+    bits = I.make_inputs(cfg)
+    dt = cfg.dtype
+    q, k, v = (to_device(bits[n], dt) for n in ("q", "k", "v"))
+    m, p, do = to_device(bits["mask_bias"], dt), to_device(bits["pair_bias"], dt), to_device(bits["dout"], dt)
+    out, lse = attn_fwd(q, k, v, m, p)
+    g = attn_bwd(q, k, v, m, p, out, lse, do, want_dmask=False, want_dpair=False)
+    torch.cuda.synchronize()
+    assert g["dmask"] is None and g["dpair"] is None
+    x = I.as_float64(bits, dt)
+    g_ref = O.attention_bwd(x["q"], x["k"], x["v"], x["mask_bias"], x["pair_bias"], x["dout"])
+    tol = TOL[dt]["grad"]
+    for key in ("dq", "dk", "dv"):
+        err = max_err(to_f64(g[key]), g_ref[key])
+        print(f"  {key} err {err:.2e}", flush=True)
+        assert err <= tol, (key, err)
 
 
 def _sample(n_total, k, seed):
