@@ -65,6 +65,8 @@ evo_status_t parse_shape(const int64_t* shape, int dtype, Shape* s) {
   if (elems > 1e12 || pair > 1e12) return EVO_ERR_BAD_SHAPE;
   const double wgs = (double)s->B * s->N * s->H * ((s->L + 31) / 32);
   if (wgs > 2.0e9) return EVO_ERR_BAD_SHAPE;
+  // the tile copies address a slice with 32-bit byte offsets
+  if ((double)s->L * s->H * s->D * 2 >= 2147483648.0) return EVO_ERR_BAD_SHAPE;
   return EVO_OK;
 }
 

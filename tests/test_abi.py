@@ -40,6 +40,8 @@ def test_status_strings():
     ((0, 2, 32, 2, 32), 0, 2),    # empty dim
     ((1, 2, -3, 2, 32), 1, 2),
     ((1, 2, 32, 2, 32), 2, 3),    # dtype
+    ((1, 2, 65537, 2, 32), 0, 2),  # L beyond 65536
+    ((1, 1, 65536, 512, 64), 0, 2),  # one slice past 2 GiB (32-bit tile offsets)
 ])
 def test_argument_errors_are_reported_before_any_device_call(shape, dtype, code):
     # these fail in shape/dtype parsing, before the library touches the device
