@@ -107,43 +107,7 @@ Range rng(const void* p, int64_t bytes) {
   return Range{lo, lo ? lo + (uintptr_t)bytes : 0};
 }
 
-// ---- 16-bit encodings of sqrt(D) = hi + lo with hi <= sqrt(D) and lo >= 0
 
-uint16_t f32_to_f16_bits(float x) {
-  _Float16 h = (_Float16)x;
-  uint16_t b;
-  std::memcpy(&b, &h, 2);
-  return b;
-}
-float f16_bits_to_f32(uint16_t b) {
-  _Float16 h;
-  std::memcpy(&h, &b, 2);
-  return (float)h;
-}
-uint16_t f32_to_bf16_bits(float x) {
-  uint32_t u;
-  std::memcpy(&u, &x, 4);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-float bf16_bits_to_f32(uint16_t b) {
-  uint32_t u = (uint32_t)b << 16;
-  float f;
-  std::memcpy(&f, &u, 4);
-  return f;
-}
-
-void sqrt_split(int64_t D, bool bf16, uint16_t* hi, uint16_t* lo) {
-  const double r = std::sqrt((double)D);
-  auto enc = [bf16](double x) { return bf16 ? f32_to_bf16_bits((float)x) : f32_to_f16_bits((float)x); };
-  auto dec = [bf16](uint16_t b) { return (double)(bf16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b)); };
-  uint16_t h = enc(r);
-  if (dec(h) > r) h = (uint16_t)(h - 1);  // positive values: one step down in the encoding
-  const double rem = r - dec(h);
-  uint16_t l = rem > 0 ? enc(rem) : (uint16_t)0;
-  *hi = h;
-  *lo = l;
-}
 
 int env_int(const char* name, int dflt) {
   const char* s = std::getenv(name);
@@ -344,7 +308,7 @@ evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const voi
   a.H = (int)s.H;
   a.G = plan_fwd_group(s);
   a.scale = (float)(1.0 / std::sqrt((double)s.D));
-  sqrt_split(s.D, dtype == EVO_BF16, &a.s_hi, &a.s_lo);
+  a.sqrt_d = (float)std::sqrt((double)s.D);
   hipError_t e = evo::launch_fwd(a, (int)s.D, dtype == EVO_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? EVO_OK : EVO_ERR_LAUNCH;
 }
@@ -433,7 +397,6 @@ evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const voi
   a.n_groups_k = (int)((s.N + a.Gk - 1) / a.Gk);
   a.sqrt_d = (float)std::sqrt((double)s.D);
   a.scale = (float)(1.0 / std::sqrt((double)s.D));
-  sqrt_split(s.D, dtype == EVO_BF16, &a.s_hi, &a.s_lo);
   hipError_t e = evo::launch_bwd(a, (int)s.D, dtype == EVO_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? EVO_OK : EVO_ERR_LAUNCH;
 }

@@ -18,9 +18,10 @@
 //   The pair bias does not depend on n.  When a row of it fits in registers
 //   (L <= 256) each wave loads its 32 rows once and reuses them for all G
 //   slices; otherwise it is re-read from L2 for every block.
-//   The mask bias enters the QK^T product itself: K gets extra columns holding
-//   mask[j] and Q gets sqrt(D) split into two 16-bit parts, so the MFMA adds
-//   mask[j]*sqrt(D), which the scale turns back into mask[j].
+//   The mask bias is the QK^T product's accumulator input: per tile an fp32
+//   row of sqrt(D)*mask[j] (-inf for keys past L) sits in LDS, and each block
+//   starts its S^T accumulator from it, so the scale turns it back into
+//   mask[j] at no VALU or extra MFMA cost.
 //   Running max: the exponent base is only moved when a row's block max
 //   exceeds it by more than 8 (log2 units), so exp values stay below 2^8 and
 //   the accumulator is rarely rescaled.
@@ -34,34 +35,11 @@ constexpr int kFwdWaves = 4;
 constexpr int kFwdRows = 32 * kFwdWaves;  // query rows per workgroup
 constexpr float kTauNat = 5.545177444479562f;  // 8 * ln 2
 
-template <int D, bool HAS_MASK>
-struct FwdShape {
-  static constexpr int KSTEPS_D = (D + 15) / 16;
-  static constexpr bool AUG_IN_PAD = (D % 16) != 0;
-  static constexpr int KSTEPS = KSTEPS_D + ((HAS_MASK && !AUG_IN_PAD) ? 1 : 0);
-  static constexpr int KW = KSTEPS * 16;  // logical K/Q row width incl. mask columns
-  static constexpr int KS = padded_stride_elems(KW);
-  static constexpr int VW = D < 32 ? 32 : D;  // columns the transposed reads touch
-  static constexpr int VS = (VW == 64) ? 80 : VW;
-  static constexpr int MB = (D + 31) / 32;  // 32-row blocks of O^T
-};
-
-// Load 8 consecutive 16-bit values of a global row; columns >= D come from the
-// mask-augmentation pattern (or zero).
 template <int D>
-__device__ __forceinline__ short8_t load_q8(const uint16_t* row, int c, bool valid, uint16_t s_hi, uint16_t s_lo,
-                                            bool has_mask) {
-  short8_t r = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (c + 8 <= D) {
-    if (valid) r = *reinterpret_cast<const short8_t*>(row + c);
-  } else if (has_mask) {
-    for (int e = 0; e < 8; ++e) {
-      int a = c + e - D;
-      r[e] = (short)(a == 0 ? s_hi : (a == 1 ? s_lo : 0));
-    }
-  }
-  return r;
-}
+struct FwdShape {
+  static constexpr int KSTEPS_D = (D + 15) / 16;  // 16-wide k-steps over d (zero past D)
+  static constexpr int MB = (D + 31) / 32;        // 32-row blocks of O^T
+};
 
 // Pair-bias values for one 32-key block in the S^T accumulator layout:
 // lane (query i) gets pair[i][j0 + 8q + 4*(l/32) + u], q,u = 0..3, packed two per dword.
@@ -94,13 +72,14 @@ __device__ __forceinline__ uint16_t pick16(const u32x2 (&b)[4], int r) {
 
 template <class T, int D, bool HAS_MASK, bool HAS_PAIR, int RES>
 __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
-  using S = FwdShape<D, HAS_MASK>;
+  using S = FwdShape<D>;
   using TL = KVTile<D>;
   // two K/V tile buffers; with a resident pair bias the same bytes first hold
   // the workgroup's 128 x (32 RES) bias slab
   constexpr int kSlab = RES > 0 ? kFwdRows * RES * 64 : 0;
   constexpr int kSmem = 2 * TL::BUF_BYTES > kSlab ? 2 * TL::BUF_BYTES : kSlab;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+  __shared__ __attribute__((aligned(16))) float smk[2][TL::CH];  // sqrt(D) * mask per key, -inf past L
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -168,17 +147,8 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
     }
   }
 
-  // constant mask-augmentation operand of Q: {s_hi, s_lo} in the k-slots after D
-  short8_t qaug = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (HAS_MASK && half == 0) {
-    qaug[0] = (short)a.s_hi;
-    qaug[1] = (short)a.s_lo;
-  }
-
   short8_t qop[S::KSTEPS_D], qnext[S::KSTEPS_D];
-  // mask values (one per dword so that a prefetched value is never repacked,
-  // which would force an early wait on the loads still in flight)
-  uint32_t mcur[TL::CH / 32], mnext[TL::CH / 32];
+  uint32_t mraw = 0;  // this thread's mask value for the next tile (thread < CH)
 
   auto load_q = [&](short8_t (&dst)[S::KSTEPS_D], int n) {
     const size_t slice = ((size_t)b * N + n) * L;
@@ -187,29 +157,23 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
     for (int s = 0; s < S::KSTEPS_D; ++s) {
       const int c = 16 * s + 8 * half;
       short8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (c + 8 <= D) {
-        v = *reinterpret_cast<const short8_t*>(qrow + c);
-      } else {
-        v = qaug;  // D = 8: the upper k-slots carry the mask augmentation (or zeros)
-        if (HAS_MASK) {
-          v[0] = (short)a.s_hi;
-          v[1] = (short)a.s_lo;
-        }
-      }
+      if (c + 8 <= D) v = *reinterpret_cast<const short8_t*>(qrow + c);
       dst[s] = v;
     }
   };
-  // Raw mask values of this lane's key in each block (keys past L read key
-  // L-1).  HAS_MASK also covers rows whose length is not a multiple of 32
-  // without a user mask: the mask is then zero, and keys past L get -inf
-  // through the same extra k-step (see qk_block), so no per-score tail test
-  // is needed anywhere.
-  auto load_mask = [&](uint32_t (&dst)[TL::CH / 32], int n, int kc0) {
+  // The mask row of a tile: thread tid loads key kc0 + tid (clamped), and
+  // after the tile's blocks it stores sqrt(D) * mask, or -inf for keys past L.
+  // HAS_MASK also covers rows whose length is not a multiple of 32 without a
+  // user mask: the mask is then zero and only the tail is -inf, so no
+  // per-score tail test is needed anywhere.
+  auto load_mask = [&](int n, int kc0) {
     if constexpr (HAS_MASK) {
-      const uint16_t* mrow = a.mask + ((size_t)b * N + n) * L;
-#pragma unroll
-      for (int jb = 0; jb < TL::CH / 32; ++jb)
-        dst[jb] = a.mask ? mrow[min(kc0 + jb * 32 + (lane & 31), L - 1)] : 0u;
+      if (tid < TL::CH) mraw = a.mask ? a.mask[((size_t)b * N + n) * L + min(kc0 + tid, L - 1)] : 0u;
+    }
+  };
+  auto store_mask = [&](int buf, int kc0) {
+    if constexpr (HAS_MASK) {
+      if (tid < TL::CH) smk[buf][tid] = (kc0 + tid < L) ? T::to_f32((uint16_t)mraw) * a.sqrt_d : kNegInf;
     }
   };
   // issue the asynchronous copy of tile t into LDS buffer (t & 1)
@@ -255,37 +219,41 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       }
     }
   };
-  // ---- S^T block = K Q^T for 32 keys (mask via the extra k-step)
-  auto qk_block = [&](const short8_t (&kop_in)[S::KSTEPS_D], const uint32_t mraw, const int j0) -> floatx16 {
-    const uint32_t mj = (j0 + (lane & 31) < L) ? mraw : (uint32_t)T::kNegInfBits;
-    floatx16 acc = floatx16{};
+  // ---- mask term of one 32-key block in the S^T accumulator layout: lane
+  // (query, half) register r holds key 8 (r / 4) + 4 half + r % 4.  Ordinary
+  // (compiler-visible) loads: the values become an MFMA accumulator input, and
+  // the compiler must see these writes to keep them clear of the MFMAs still
+  // reading the previous block's input from the same registers.
+  auto mc_fetch = [&](int buf, const int jb, floatx16& dst) {
+    if constexpr (HAS_MASK) {
+      const float* row = &smk[buf][jb * 32 + 4 * half];
 #pragma unroll
-    for (int s = 0; s < S::KSTEPS_D; ++s) {
-      short8_t kop = kop_in[s];
-      if (2 * s + half >= TL::KC && HAS_MASK) {  // D = 8, upper k-slots: mask augmentation
-        kop[0] = (short)mj;
-        kop[1] = (short)(a.s_lo != 0 ? mj : 0);
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 v = *reinterpret_cast<const floatx4*>(row + 8 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[4 * q + e] = v[e];
       }
-      acc = T::mfma(kop, qop[s], acc);
     }
-    if constexpr (HAS_MASK && (D % 16) == 0) {
-      short8_t ka = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (half == 0) {
-        ka[0] = (short)mj;
-        ka[1] = (short)(a.s_lo != 0 ? mj : 0);
-      }
-      acc = T::mfma(ka, qaug, acc);
-    }
+  };
+  // ---- S^T block = K Q^T + sqrt(D) mask for 32 keys
+  auto qk_block = [&](const short8_t (&kop_in)[S::KSTEPS_D], const floatx16& minit) -> floatx16 {
+    floatx16 acc = HAS_MASK ? minit : floatx16{};
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS_D; ++s) acc = T::mfma(kop_in[s], qop[s], acc);
     return acc;
   };
 
   // ---- bias, online softmax and O^T += V^T P^T for one block whose scores are in acc
-  auto softmax_pv = [&](const floatx16& acc, const uint8_t* buf, const int jb, const int j0, const u32x2 (&pb)[4],
-                        short8_t (&kpre)[S::KSTEPS_D], const int jb_pre) {
+  auto softmax_pv = [&](const floatx16& acc, const int tb, const int jb, const u32x2 (&pb)[4],
+                        short8_t (&kpre)[S::KSTEPS_D], floatx16& mpre, const int jb_pre) {
+    const uint8_t* buf = smem + tb * TL::BUF_BYTES;
     const uint8_t* vb = buf + TL::KCH * 16;
     // V^T operands first: the reads complete under the softmax VALU work
-    // K operands two blocks ahead, completed by the wait below
-    if (jb_pre >= 0) k_fetch(buf, jb_pre, kpre);
+    // K operands and the mask term two blocks ahead, completed by the wait below
+    if (jb_pre >= 0) {
+      k_fetch(buf, jb_pre, kpre);
+      mc_fetch(tb, jb_pre, mpre);
+    }
     const int qg = lane >> 4, i16 = lane & 15, g = qg >> 1;
     short4_t vt[4 * S::MB];  // [t][mb][lo/hi]
 #pragma unroll
@@ -347,8 +315,9 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   // ---- pipeline: tile t computes from buffer t&1 while tile t+1 streams into the other
   if (ntiles > 0) {
     issue_tile(0);
-    load_mask(mnext, n_begin, 0);
+    load_mask(n_begin, 0);
     load_q(qnext, n_begin);
+    store_mask(0, 0);
   }
   for (int t = 0; t < ntiles; ++t) {
     const int n = n_begin + t / nchunks;
@@ -356,8 +325,6 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
     const int kc0 = c * TL::CH;
     __builtin_amdgcn_s_waitcnt(0);  // this thread's copies of tile t (and its mask/Q loads) are done
     __syncthreads();                // everyone's are; everyone has finished tile t-1
-#pragma unroll
-    for (int jb = 0; jb < TL::CH / 32; ++jb) mcur[jb] = mnext[jb];
     if (c == 0) {
 #pragma unroll
       for (int s = 0; s < S::KSTEPS_D; ++s) qop[s] = qnext[s];
@@ -376,35 +343,41 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
     if (t + 1 < ntiles) {
       issue_tile(t + 1);
       const int n1 = n_begin + (t + 1) / nchunks;
-      load_mask(mnext, n1, ((t + 1) % nchunks) * TL::CH);
+      load_mask(n1, ((t + 1) % nchunks) * TL::CH);
       if ((t + 1) % nchunks == 0) load_q(qnext, n1);
     }
-    const uint8_t* buf = smem + (t & 1) * TL::BUF_BYTES;
+    const int tb = t & 1;
+    const uint8_t* buf = smem + tb * TL::BUF_BYTES;
     // blocks of the tile, software-pipelined: while block jb is in its softmax,
-    // the QK^T MFMAs of block jb+1 run and the K operands of block jb+2 load
+    // the QK^T MFMAs of block jb+1 run and the K operands and mask term of
+    // block jb+2 load
     const int nblk = min(TL::CH, L - kc0 + 31) / 32;
     {
       constexpr int NB = (RES > 0 && RES < TL::CH / 32) ? RES : TL::CH / 32;
       short8_t kreg[2][S::KSTEPS_D];
-      floatx16 sacc[2];
+      floatx16 sacc[2], mc0 = {}, mc = {};
       k_fetch(buf, 0, kreg[0]);
-      if (nblk > 1) k_fetch(buf, 1, kreg[1]);
+      mc_fetch(tb, 0, mc0);
+      if (nblk > 1) {
+        k_fetch(buf, 1, kreg[1]);
+        mc_fetch(tb, 1, mc);
+      }
       {
         short4_t none[2] = {};
         lds_wait_all(none, kreg[0]);
         lds_wait_all(none, kreg[1]);
+
       }
-      sacc[0] = qk_block(kreg[0], mcur[0], kc0);
+      sacc[0] = qk_block(kreg[0], mc0);
 #pragma unroll
       for (int jb = 0; jb < NB; ++jb) {
         if (jb < nblk) {
-          if (jb + 1 < NB && jb + 1 < nblk)
-            sacc[(jb + 1) & 1] = qk_block(kreg[(jb + 1) & 1], mcur[jb + 1], kc0 + 32 * (jb + 1));
+          if (jb + 1 < NB && jb + 1 < nblk) sacc[(jb + 1) & 1] = qk_block(kreg[(jb + 1) & 1], mc);
           const int pre = (jb + 2 < NB && jb + 2 < nblk) ? jb + 2 : -1;
           if constexpr (RES > 0) {
-            softmax_pv(sacc[jb & 1], buf, jb, jb * 32, pres[jb < RES ? jb : 0], kreg[jb & 1], pre);
+            softmax_pv(sacc[jb & 1], tb, jb, pres[jb < RES ? jb : 0], kreg[jb & 1], mc, pre);
           } else {
-            softmax_pv(sacc[jb & 1], buf, jb, kc0 + jb * 32, ptile[HAS_PAIR ? jb : 0], kreg[jb & 1], pre);
+            softmax_pv(sacc[jb & 1], tb, jb, ptile[HAS_PAIR ? jb : 0], kreg[jb & 1], mc, pre);
           }
         }
       }
@@ -449,6 +422,8 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
         }
       }
     }
+    // the next tile's mask row (its buffer was last read during tile t - 1)
+    if (t + 1 < ntiles) store_mask((t + 1) & 1, ((t + 1) % nchunks) * TL::CH);
   }
 }
 

@@ -19,7 +19,7 @@ struct FwdArgs {
   int n_groups;  // ceil(N / G)
   int i_tiles;   // query tiles per slice
   float scale;   // 1/sqrt(D)
-  uint16_t s_hi, s_lo;  // sqrt(D) = s_hi + s_lo in the 16-bit dtype, s_lo >= 0
+  float sqrt_d;  // sqrt(D) in fp32 (the mask enters the score accumulator pre-multiplied by it)
 };
 
 struct BwdArgs {
@@ -49,7 +49,6 @@ struct BwdArgs {
   int n_groups_k;
   float scale;
   float sqrt_d;    // sqrt(D) in fp32 (the masks enter the score accumulators pre-multiplied by it)
-  uint16_t s_hi, s_lo;
 };
 
 // Map a hardware workgroup id to a logical one so that consecutive logical
