@@ -188,12 +188,22 @@ __device__ __forceinline__ short8_t cat4(short4_t a, short4_t b) {
 // columns; the padding is never used).  Both are filled by
 // global_load_lds_dwordx4, which writes 64 consecutive 16-byte chunks per wave
 // instruction, so the layout is a dense array of 16-byte chunks.  Chunk c of
-// row r sits at position c ^ swz(r): 16 consecutive rows read at the same
-// column then hit 16 distinct 4-bank groups.
+// row r sits at position c ^ swz(r).  The swizzle is constant on aligned
+// groups of four rows (the transposed reads take a 4 x 4 block of 8-byte
+// pieces from four consecutive rows) and has a period of 16 rows (operand
+// blocks of 16 rows sit at fixed offsets from a lane's base address).  For
+// 64-byte rows it is -(r / 4) mod 4: measured with the 16-row operand reads of
+// the 16x16x32 MFMAs, the 32-row reads of the 32x32x16 MFMAs and both
+// transposed-read patterns, it runs every one of them at the contiguous-read
+// rate, where r / 4 mod 4 left the 16-row b128 reads at about 60 % of it.
 template <int C>
 __device__ __forceinline__ int kv_swz(int r) {
-  constexpr int R = 16 / C;  // rows per 64-dword bank cycle
-  return (r / R) % C;
+  if constexpr (C == 4) {
+    return (4 - ((r >> 2) & 3)) & 3;
+  } else {
+    constexpr int R = 16 / C;  // rows per 64-dword bank cycle
+    return (r / R) % C;
+  }
 }
 
 template <int D>

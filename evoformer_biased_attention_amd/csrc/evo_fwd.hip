@@ -206,18 +206,38 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   floatx16 oacc[S::MB];
   float m_used = kNegInf, l_part = 0.f;
 
-  // ---- K operands of one 32-key block (asm reads, completed by the next PV wait)
-  auto k_fetch = [&](const uint8_t* buf, const int jb, short8_t (&kop)[S::KSTEPS_D]) {
-    const int r = jb * 32 + (lane & 31);
+  // Per-lane byte offsets within a tile buffer.  The swizzle repeats every 16
+  // rows, so block jb of a tile adds the constant 32 jb rows, which goes into
+  // the read instruction's offset field.
+  uint32_t koff[S::KSTEPS_D];
 #pragma unroll
-    for (int s = 0; s < S::KSTEPS_D; ++s) {
-      const int c = 2 * s + half;
-      if (c < TL::KC) {
-        kop[s] = lds_read_b128_asm(buf, (r * TL::KC + (c ^ kv_swz<TL::KC>(r))) * 16);
+  for (int s = 0; s < S::KSTEPS_D; ++s) {
+    const int r = lane & 31, c = 2 * s + half;
+    koff[s] = (c < TL::KC) ? (uint32_t)((r * TL::KC + (c ^ kv_swz<TL::KC>(r))) * 16) : 0u;
+  }
+  uint32_t voff[S::MB][2];  // V^T reads of rows 4 g + i16 / 4 and 8 rows further
+  {
+    const int qg = lane >> 4, i16 = lane & 15, g = qg >> 1;
+    const int row = 4 * g + (i16 >> 2);
+#pragma unroll
+    for (int mb2 = 0; mb2 < S::MB; ++mb2) {
+      const int col = 16 * (qg & 1) + 32 * mb2 + 4 * (i16 & 3);
+      voff[mb2][0] = (uint32_t)(TL::KCH * 16 + tr_off<TL::VC>(row, col));
+      voff[mb2][1] = (uint32_t)(TL::KCH * 16 + tr_off<TL::VC>(row + 8, col));
+    }
+  }
+
+  // ---- K operands of one 32-key block (asm reads, completed by the next PV wait)
+  auto k_fetch = [&](auto jbc, const uint32_t bufa, short8_t (&kop)[S::KSTEPS_D]) {
+    constexpr int jb = decltype(jbc)::value;
+    static_for<0, S::KSTEPS_D>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if (2 * s + half < TL::KC) {
+        kop[s] = __builtin_bit_cast(short8_t, lds_b128_imm<jb * 32 * TL::KC * 16>(bufa + koff[s]));
       } else {
         kop[s] = short8_t{0, 0, 0, 0, 0, 0, 0, 0};
       }
-    }
+    });
   };
   // ---- mask term of one 32-key block in the S^T accumulator layout: lane
   // (query, half) register r holds key 8 (r / 4) + 4 half + r % 4.  Ordinary
@@ -244,28 +264,28 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   };
 
   // ---- bias, online softmax and O^T += V^T P^T for one block whose scores are in acc
-  auto softmax_pv = [&](const floatx16& acc, const int tb, const int jb, const u32x2 (&pb)[4],
-                        short8_t (&kpre)[S::KSTEPS_D], floatx16& mpre, const int jb_pre) {
-    const uint8_t* buf = smem + tb * TL::BUF_BYTES;
-    const uint8_t* vb = buf + TL::KCH * 16;
+  auto softmax_pv = [&](const floatx16& acc, const int tb, auto jbc, const u32x2 (&pb)[4],
+                        short8_t (&kpre)[S::KSTEPS_D], floatx16& mpre, auto prec, const bool pre_live) {
+    constexpr int jb = decltype(jbc)::value, jb_pre = decltype(prec)::value;
+    const uint32_t bufa = lds_addr(smem + tb * TL::BUF_BYTES);
     // V^T operands first: the reads complete under the softmax VALU work
     // K operands and the mask term two blocks ahead, completed by the wait below
-    if (jb_pre >= 0) {
-      k_fetch(buf, jb_pre, kpre);
-      mc_fetch(tb, jb_pre, mpre);
-    }
-    const int qg = lane >> 4, i16 = lane & 15, g = qg >> 1;
-    short4_t vt[4 * S::MB];  // [t][mb][lo/hi]
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int row = jb * 32 + 16 * t + 4 * g + (i16 >> 2);
-#pragma unroll
-      for (int mb2 = 0; mb2 < S::MB; ++mb2) {
-        const int col = 16 * (qg & 1) + 32 * mb2 + 4 * (i16 & 3);
-        vt[(t * S::MB + mb2) * 2 + 0] = lds_read_tr_asm(vb, tr_off<TL::VC>(row, col));
-        vt[(t * S::MB + mb2) * 2 + 1] = lds_read_tr_asm(vb, tr_off<TL::VC>(row + 8, col));
+    if constexpr (jb_pre >= 0) {
+      if (pre_live) {
+        k_fetch(prec, bufa, kpre);
+        mc_fetch(tb, jb_pre, mpre);
       }
     }
+    short4_t vt[4 * S::MB];  // [t][mb][lo/hi]
+    static_for<0, 2>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      static_for<0, S::MB>([&](auto mc_) {
+        constexpr int mb2 = decltype(mc_)::value;
+        constexpr int off = (jb * 32 + 16 * t) * TL::VC * 16;
+        vt[(t * S::MB + mb2) * 2 + 0] = lds_tr_imm<off>(bufa + voff[mb2][0]);
+        vt[(t * S::MB + mb2) * 2 + 1] = lds_tr_imm<off>(bufa + voff[mb2][1]);
+      });
+    });
     float sv[16];
     if constexpr (HAS_PAIR) {
 #pragma unroll
@@ -356,31 +376,37 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       constexpr int NB = (RES > 0 && RES < TL::CH / 32) ? RES : TL::CH / 32;
       short8_t kreg[2][S::KSTEPS_D];
       floatx16 sacc[2], mc0 = {}, mc = {};
-      k_fetch(buf, 0, kreg[0]);
+      const uint32_t bufa = lds_addr(buf);
+      k_fetch(std::integral_constant<int, 0>{}, bufa, kreg[0]);
       mc_fetch(tb, 0, mc0);
       if (nblk > 1) {
-        k_fetch(buf, 1, kreg[1]);
+        k_fetch(std::integral_constant<int, 1>{}, bufa, kreg[1]);
         mc_fetch(tb, 1, mc);
       }
       {
         short4_t none[2] = {};
         lds_wait_all(none, kreg[0]);
         lds_wait_all(none, kreg[1]);
-
       }
       sacc[0] = qk_block(kreg[0], mc0);
-#pragma unroll
-      for (int jb = 0; jb < NB; ++jb) {
+      static_for<0, NB>([&](auto jbc) {
+        constexpr int jb = decltype(jbc)::value;
         if (jb < nblk) {
-          if (jb + 1 < NB && jb + 1 < nblk) sacc[(jb + 1) & 1] = qk_block(kreg[(jb + 1) & 1], mc);
-          const int pre = (jb + 2 < NB && jb + 2 < nblk) ? jb + 2 : -1;
+          if constexpr (jb + 1 < NB) {
+            if (jb + 1 < nblk) sacc[(jb + 1) & 1] = qk_block(kreg[(jb + 1) & 1], mc);
+          }
+          // the K operands of block jb + 2 are read only when it exists
+          const bool pre_live = jb + 2 < nblk;
+          constexpr int jpre = jb + 2 < NB ? jb + 2 : -1;
           if constexpr (RES > 0) {
-            softmax_pv(sacc[jb & 1], tb, jb, pres[jb < RES ? jb : 0], kreg[jb & 1], mc, pre);
+            softmax_pv(sacc[jb & 1], tb, jbc, pres[jb < RES ? jb : 0], kreg[jb & 1], mc,
+                       std::integral_constant<int, jpre>{}, pre_live);
           } else {
-            softmax_pv(sacc[jb & 1], tb, jb, ptile[HAS_PAIR ? jb : 0], kreg[jb & 1], mc, pre);
+            softmax_pv(sacc[jb & 1], tb, jbc, ptile[HAS_PAIR ? jb : 0], kreg[jb & 1], mc,
+                       std::integral_constant<int, jpre>{}, pre_live);
           }
         }
-      }
+      });
     }
     if (c == nchunks - 1) {
       // ---- epilogue of slice n: normalise, store O and lse
