@@ -263,6 +263,7 @@ def main():
         return e0.elapsed_time(e1) / args.steps
 
     ms_fwd = timed_graph(lambda: attn_fwd(q, k, v, m, p))
+    ms_fwd_inf = timed_graph(lambda: attn_fwd(q, k, v, m, p, need_lse=False))
     ms_bwd = timed_graph(lambda: attn_bwd(q, k, v, m, p, out, lse, do, workspace=ws))
 
     # ---- per-kernel launch times: HIP events the library records on this
@@ -353,6 +354,8 @@ def main():
         "timing": "HIP graph replay of the captured step (launch-cost free); eager Python loop also reported",
         "ms_per_step_eager": round(ms_eager, 5),
         "fwd": {"ms": round(ms_fwd, 5), "tflops": round(tf_fwd, 2), "pct_peak": round(100 * tf_fwd / PEAK_MFMA_TFLOPS, 2)},
+        "fwd_inference": {"ms": round(ms_fwd_inf, 5), "tflops": round(tf_fwd * ms_fwd / ms_fwd_inf, 2),
+                          "note": "forward with no lse kept (no backward follows)"},
         "bwd": {"ms": round(ms_bwd, 5), "tflops": round(tf_bwd, 2), "pct_peak": round(100 * tf_bwd / PEAK_MFMA_TFLOPS, 2)},
         "kernels": {n: {"avg_us": round(v_["avg_us"], 2), "launches": v_["launches"], "share": round(v_["share"], 3)}
                     for n, v_ in kernels.items()},

@@ -42,17 +42,22 @@ def _check_inputs(q, k, v, mask, pair):
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_bias: Optional[torch.Tensor] = None,
-             pair_bias: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Forward: returns (out [B,N,L,H,D] dtype, lse [B,N,H,L] float32)."""
+             pair_bias: Optional[torch.Tensor] = None, need_lse: bool = True
+             ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Forward: returns (out [B,N,L,H,D] dtype, lse [B,N,H,L] float32).
+
+    With ``need_lse=False`` (inference: no backward follows) the lse is neither
+    allocated nor written and None is returned in its place; out is identical.
+    """
     _check_inputs(q, k, v, mask_bias, pair_bias)
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
     mask_bias = None if mask_bias is None else mask_bias.contiguous()
     pair_bias = None if pair_bias is None else pair_bias.contiguous()
     B, N, L, H, D = q.shape
     out = torch.empty_like(q)
-    lse = torch.empty((B, N, H, L), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, N, H, L), dtype=torch.float32, device=q.device) if need_lse else None
     _lib.check(_lib.evo_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(mask_bias), _ptr(pair_bias),
-                                 out.data_ptr(), lse.data_ptr(), q.shape, _DT[q.dtype], _stream()))
+                                 out.data_ptr(), _ptr(lse), q.shape, _DT[q.dtype], _stream()))
     return out, lse
 
 
@@ -124,6 +129,9 @@ def evoformer_attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
         raise ValueError("at most two biases: [B,N,1,1,L] and [B,1,H,L,L]")
     while len(bl) < 2:
         bl.append(None)
+    if not (torch.is_grad_enabled() and any(t is not None and t.requires_grad for t in (Q, K, V, *bl))):
+        # no gradient can flow: the inference forward, which keeps no lse
+        return attn_fwd(Q, K, V, bl[0], bl[1], need_lse=False)[0]
     return EvoformerFusedAttention.apply(Q, K, V, bl[0], bl[1])
 
 

@@ -281,7 +281,8 @@ evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const voi
   Shape s;
   evo_status_t st = parse_shape(shape, dtype, &s);
   if (st != EVO_OK) return st;
-  if (!q || !k || !v || !out || !lse) return EVO_ERR_NULL_POINTER;
+  // lse may be NULL: a forward with no backward after it (inference)
+  if (!q || !k || !v || !out) return EVO_ERR_NULL_POINTER;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return EVO_ERR_DEVICE;
   if (!device_is_gfx950(dev)) return EVO_ERR_DEVICE;

@@ -442,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
             const int d = 32 * mb2 + 8 * (q + half);
             if (i_valid && d < D) *reinterpret_cast<u32x4*>(orow + d) = w;
           }
-        if (i_valid && half == 0) {
+        if (i_valid && half == 0 && a.lse != nullptr) {
           const float lse = (m_used == kNegInf || !(l_tot > 0.f)) ? kNegInf : m_used + __logf(l_tot);
           a.lse[(((size_t)b * N + n) * H + h) * L + i] = lse;
         }

@@ -66,8 +66,11 @@ typedef enum {
  *   mask_bias   [B,N,1,1,L] dtype or NULL  additive bias on keys, shared by all heads and queries
  *   pair_bias   [B,1,H,L,L] dtype or NULL  additive bias, shared by every n
  *   out         [B,N,L,H,D] dtype          output
- *   lse         [B,N,H,L]   float32        natural-log log-sum-exp of each row of S
- * A query row whose scores are all -inf gets out = 0 and lse = -inf. */
+ *   lse         [B,N,H,L]   float32        natural-log log-sum-exp of each row of S, or NULL
+ * A query row whose scores are all -inf gets out = 0 and lse = -inf.  With lse NULL the
+ * call is a forward for inference (the guide's §3.2 notes the forward kernels pay off
+ * at inference for every attention type): out is the same, bit for bit, and nothing is
+ * kept for a backward. */
 evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const void* mask_bias,
                           const void* pair_bias, void* out, float* lse, const int64_t shape[5],
                           int dtype, void* stream);

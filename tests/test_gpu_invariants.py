@@ -3,8 +3,10 @@ error behaviour on a real device.
 
 * masked keys: changing K and V at keys whose mask is -1e9 changes no output
   bit; dK, dV and dmask are exactly zero there (P is exactly zero at those keys);
-* determinism: two runs give the same bits (every path with L <= 768; longer
-  rows sum dpair with atomics and are excluded);
+* determinism: two runs give the same bits (every path, rows longer than one
+  key tile included: every reduction runs in a fixed order, no atomics);
+* inference forward (no lse kept): the same output bits as the forward that
+  keeps the lse, through the C ABI and through the no-grad Python call;
 * coverage: outputs pre-filled with NaN come back finite (every element written);
 * guard bands: bytes just before and after every output and the workspace are
   left untouched;
@@ -165,6 +167,29 @@ def test_autograd_wrapper_equals_direct_calls():
     out_m = evoformer_attention(x["q"], x["k"], x["v"], [x["mask_bias"]])
     o3, _ = attn_fwd(x["q"], x["k"], x["v"], x["mask_bias"], None)
     assert torch.equal(out_m, o3)
+
+
+@pytest.mark.parametrize("cfg", [CASES[0], CASES[2], CASES[4], CASES[5]], ids=[c.name for c in (CASES[0], CASES[2], CASES[4], CASES[5])])
+def test_inference_forward_same_output(cfg):
+    from evoformer_biased_attention_amd.attention import attn_fwd, evoformer_attention
+
+    print(f"case inference fwd {cfg.name} shape={cfg.shape} dtype={cfg.dtype}", flush=True)
+    _, x = _inputs(cfg)
+    ref, lse = attn_fwd(x["q"], x["k"], x["v"], x["mask_bias"], x["pair_bias"])
+    raw, body = _guarded(cfg.shape, x["q"].dtype, 0xFF)
+    st = _lib.evo_attn_fwd(x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr(), _ptr(x["mask_bias"]),
+                           _ptr(x["pair_bias"]), body.data_ptr(), None, cfg.shape, DT[cfg.dtype],
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(body, ref), "out differs when no lse is kept"
+    nb = body.numel() * body.element_size()
+    assert bool((raw[:GUARD] == 0xFF).all()) and bool((raw[GUARD + nb:] == 0xFF).all())
+    out2, none = attn_fwd(x["q"], x["k"], x["v"], x["mask_bias"], x["pair_bias"], need_lse=False)
+    assert none is None and torch.equal(out2, ref)
+    with torch.no_grad():
+        out3 = evoformer_attention(x["q"], x["k"], x["v"], [x["mask_bias"], x["pair_bias"]])
+    assert torch.equal(out3, ref)
 
 
 # ---- argument errors on a real device ----
