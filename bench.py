@@ -264,6 +264,12 @@ def main():
 
     ms_fwd = timed_graph(lambda: attn_fwd(q, k, v, m, p))
     ms_fwd_inf = timed_graph(lambda: attn_fwd(q, k, v, m, p, need_lse=False))
+    # the same step on views transposed over N and L (the layout of triangle
+    # attention around the ending node, taken without a copy)
+    qt, kt, vt, dot = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v, do))
+    out_t, lse_t = attn_fwd(qt, kt, vt, m, p)
+    ms_step_t = timed_graph(lambda: attn_bwd(qt, kt, vt, m, p, *attn_fwd(qt, kt, vt, m, p), dot, workspace=ws))
+    del qt, kt, vt, dot, out_t, lse_t
     ms_bwd = timed_graph(lambda: attn_bwd(q, k, v, m, p, out, lse, do, workspace=ws))
 
     # ---- per-kernel launch times: HIP events the library records on this
@@ -356,6 +362,8 @@ def main():
         "fwd": {"ms": round(ms_fwd, 5), "tflops": round(tf_fwd, 2), "pct_peak": round(100 * tf_fwd / PEAK_MFMA_TFLOPS, 2)},
         "fwd_inference": {"ms": round(ms_fwd_inf, 5), "tflops": round(tf_fwd * ms_fwd / ms_fwd_inf, 2),
                           "note": "forward with no lse kept (no backward follows)"},
+        "step_transposed_layout": {"ms": round(ms_step_t, 5), "tflops": round(tf_step * ms_step / ms_step_t, 2),
+                                   "note": "fwd+bwd on Q, K, V, dO views transposed over N and L (no copy)"},
         "bwd": {"ms": round(ms_bwd, 5), "tflops": round(tf_bwd, 2), "pct_peak": round(100 * tf_bwd / PEAK_MFMA_TFLOPS, 2)},
         "kernels": {n: {"avg_us": round(v_["avg_us"], 2), "launches": v_["launches"], "share": round(v_["share"], 3)}
                     for n, v_ in kernels.items()},

@@ -18,6 +18,8 @@ EVO_BF16 = 1
 EXPORTED = (
     "evo_attn_fwd",
     "evo_attn_bwd",
+    "evo_attn_fwd_strided",
+    "evo_attn_bwd_strided",
     "evo_attn_bwd_workspace_bytes",
     "evo_attn_bwd_workspace_offsets",
     "evo_status_string",
@@ -50,6 +52,10 @@ def load() -> ctypes.CDLL:
     lib.evo_attn_fwd.restype = I
     lib.evo_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, S, I, P]
     lib.evo_attn_bwd.restype = I
+    lib.evo_attn_fwd_strided.argtypes = [P, P, P, P, P, P, P, S, S, I, P]
+    lib.evo_attn_fwd_strided.restype = I
+    lib.evo_attn_bwd_strided.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, S, S, I, P]
+    lib.evo_attn_bwd_strided.restype = I
     lib.evo_attn_bwd_workspace_bytes.argtypes = [S, I, I, I]
     lib.evo_attn_bwd_workspace_bytes.restype = Z
     lib.evo_attn_bwd_workspace_offsets.argtypes = [S, I, I, I, ctypes.POINTER(Z), ctypes.POINTER(Z), ctypes.POINTER(Z)]
@@ -83,6 +89,22 @@ def evo_attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmas
                  workspace, workspace_bytes, shape, dtype, stream) -> int:
     return load().evo_attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias,
                                dpair_bias, workspace, workspace_bytes, shape_arg(shape), dtype, stream)
+
+
+def strides_arg(strides):
+    return None if strides is None else (ctypes.c_int64 * 3)(*[int(x) for x in strides])
+
+
+def evo_attn_fwd_strided(q, k, v, mask_bias, pair_bias, out, lse, shape, strides, dtype, stream) -> int:
+    return load().evo_attn_fwd_strided(q, k, v, mask_bias, pair_bias, out, lse, shape_arg(shape),
+                                       strides_arg(strides), dtype, stream)
+
+
+def evo_attn_bwd_strided(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias,
+                         workspace, workspace_bytes, shape, strides, dtype, stream) -> int:
+    return load().evo_attn_bwd_strided(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias,
+                                       dpair_bias, workspace, workspace_bytes, shape_arg(shape),
+                                       strides_arg(strides), dtype, stream)
 
 
 def evo_attn_bwd_workspace_bytes(shape, dtype, has_mask, has_pair) -> int:

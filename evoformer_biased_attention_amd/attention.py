@@ -41,6 +41,37 @@ def _check_inputs(q, k, v, mask, pair):
         raise ValueError(f"bias 2 must be [B,1,H,L,L] = {(B, 1, H, L, L)}, got {tuple(pair.shape)}")
 
 
+def _layout(ts) -> Optional[Tuple[int, int, int]]:
+    """The (sB, sN, sL) element strides that the [B,N,L,H,D] tensors ``ts`` share,
+    when the library can take them as they are: the same strides for all, the
+    H heads of D elements of each row dense, and the tensor dense as a whole
+    (a permutation of the B, N, L dims, such as a view transposed over N and L).
+    None otherwise (the caller then makes the tensors contiguous)."""
+    t0 = ts[0]
+    B, N, L, H, D = t0.shape
+    if all(t.is_contiguous() for t in ts):
+        return _dense_strides(t0.shape)
+    st = t0.stride()
+    if any(t.stride() != st for t in ts[1:]):
+        return None
+    if st[4] != 1 or (H > 1 and st[3] != D):
+        return None
+    # dense as a whole: the dims of extent > 1, in increasing stride order, each
+    # start where the ones below end (the first right after one row of H * D)
+    span = H * D
+    for x, e in sorted((x, e) for x, e in zip(st[:3], (B, N, L)) if e > 1):
+        if x != span:
+            return None
+        span = x * e
+    # a dim of extent 1 may carry any stride: give it one the library accepts
+    return tuple(x if e > 1 else 8 for x, e in zip(st[:3], (B, N, L)))
+
+
+def _dense_strides(shape) -> Tuple[int, int, int]:
+    B, N, L, H, D = shape
+    return (N * L * H * D, L * H * D, H * D)
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_bias: Optional[torch.Tensor] = None,
              pair_bias: Optional[torch.Tensor] = None, need_lse: bool = True
              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
@@ -50,14 +81,18 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_bias: Optio
     allocated nor written and None is returned in its place; out is identical.
     """
     _check_inputs(q, k, v, mask_bias, pair_bias)
-    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    lay = _layout((q, k, v))
+    if lay is None:
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        lay = _dense_strides(q.shape)
     mask_bias = None if mask_bias is None else mask_bias.contiguous()
     pair_bias = None if pair_bias is None else pair_bias.contiguous()
     B, N, L, H, D = q.shape
-    out = torch.empty_like(q)
+    out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, N, H, L), dtype=torch.float32, device=q.device) if need_lse else None
-    _lib.check(_lib.evo_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(mask_bias), _ptr(pair_bias),
-                                 out.data_ptr(), _ptr(lse), q.shape, _DT[q.dtype], _stream()))
+    _lib.check(_lib.evo_attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(mask_bias),
+                                         _ptr(pair_bias), out.data_ptr(), _ptr(lse), q.shape, lay, _DT[q.dtype],
+                                         _stream()))
     return out, lse
 
 
@@ -65,22 +100,27 @@ def attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask: bool = T
              workspace: Optional[torch.Tensor] = None) -> Dict[str, Optional[torch.Tensor]]:
     """Backward: returns dict dq, dk, dv, dmask (or None), dpair (or None), workspace."""
     _check_inputs(q, k, v, mask_bias, pair_bias)
-    q, k, v, out, dout = (t.contiguous() for t in (q, k, v, out, dout))
+    lay = _layout((q, k, v, out))
+    if lay is None:
+        q, k, v, out = (t.contiguous() for t in (q, k, v, out))
+        lay = _dense_strides(q.shape)
+    if dout.stride() != q.stride():
+        dout = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device).copy_(dout)
     lse = lse.contiguous()
     mask_bias = None if mask_bias is None else mask_bias.contiguous()
     pair_bias = None if pair_bias is None else pair_bias.contiguous()
     B, N, L, H, D = q.shape
     dt = _DT[q.dtype]
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) for _ in range(3))
     dmask = torch.empty_like(mask_bias) if (mask_bias is not None and want_dmask) else None
     dpair = torch.empty_like(pair_bias) if (pair_bias is not None and want_dpair) else None
     nbytes = _lib.evo_attn_bwd_workspace_bytes(q.shape, dt, mask_bias is not None, pair_bias is not None)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-    _lib.check(_lib.evo_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(mask_bias), _ptr(pair_bias),
-                                 out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                                 dv.data_ptr(), _ptr(dmask), _ptr(dpair), workspace.data_ptr(), workspace.numel(),
-                                 q.shape, dt, _stream()))
+    _lib.check(_lib.evo_attn_bwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(mask_bias),
+                                         _ptr(pair_bias), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(dmask), _ptr(dpair),
+                                         workspace.data_ptr(), workspace.numel(), q.shape, lay, dt, _stream()))
     return {"dq": dq, "dk": dk, "dv": dv, "dmask": dmask, "dpair": dpair, "workspace": workspace}
 
 

@@ -70,6 +70,51 @@ evo_status_t parse_shape(const int64_t* shape, int dtype, Shape* s) {
   return EVO_OK;
 }
 
+// Element strides of dims B, N, L shared by the [B,N,L,H,D] tensors of a call
+// (the H heads of D elements of one row are dense).  strides == nullptr: the
+// dense layout.  Rows are 16-byte aligned (strides in multiples of 8
+// elements), no two (b, n, l) rows overlap (over the dims of extent > 1 taken
+// in increasing stride order, each stride covers the span of the ones below
+// it, the first at least one row of H * D), and a (b, n) slice spans less
+// than 2 GiB (the tile copies use 32-bit byte offsets).
+struct Layout {
+  int64_t sB, sN, sL;
+};
+
+evo_status_t parse_layout(const Shape& s, const int64_t* strides, Layout* lay) {
+  const int64_t hd = s.H * s.D;
+  if (strides == nullptr) {
+    lay->sL = hd;
+    lay->sN = s.L * hd;
+    lay->sB = s.N * s.L * hd;
+    return EVO_OK;
+  }
+  const int64_t st[3] = {strides[0], strides[1], strides[2]};
+  const int64_t ext[3] = {s.B, s.N, s.L};
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 1 || st[i] > ((int64_t)1 << 40) || st[i] % 8 != 0) return EVO_ERR_BAD_STRIDES;
+  int order[3] = {0, 1, 2};
+  std::stable_sort(order, order + 3, [&](int x, int y) { return st[x] < st[y]; });
+  double span = (double)hd;
+  for (int k : order) {
+    if (ext[k] == 1) continue;
+    if ((double)st[k] < span) return EVO_ERR_BAD_STRIDES;
+    span = (double)st[k] * (double)ext[k];
+  }
+  if ((double)(s.L - 1) * st[2] * 2 + (double)hd * 2 >= 2147483648.0) return EVO_ERR_BAD_STRIDES;
+  const double foot = ((double)(s.B - 1) * st[0] + (double)(s.N - 1) * st[1] + (double)(s.L - 1) * st[2] + hd) * 2;
+  if (foot > 1.0e15) return EVO_ERR_BAD_STRIDES;
+  lay->sB = st[0];
+  lay->sN = st[1];
+  lay->sL = st[2];
+  return EVO_OK;
+}
+
+// bytes from the first to one past the last element of a [B,N,L,H,D] tensor
+int64_t footprint_bytes(const Shape& s, const Layout& l) {
+  return ((s.B - 1) * l.sB + (s.N - 1) * l.sN + (s.L - 1) * l.sL + s.H * s.D) * 2;
+}
+
 evo_status_t check_device_ptr(const void* p, int dev) {
   if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return EVO_ERR_ALIGNMENT;
   hipPointerAttribute_t attr;
@@ -272,15 +317,24 @@ const char* evo_status_string(int status) {
     case EVO_ERR_DEVICE: return "the current device is not gfx950 (MI355X)";
     case EVO_ERR_LAUNCH: return "kernel launch failed";
     case EVO_ERR_ALIAS: return "an output overlaps an input or another output";
+    case EVO_ERR_BAD_STRIDES: return "strides: not multiples of 8 elements, overlapping rows, or a slice past 2 GiB";
   }
   return "unknown status";
 }
 
 evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const void* mask_bias, const void* pair_bias,
                           void* out, float* lse, const int64_t shape[5], int dtype, void* stream) {
+  return evo_attn_fwd_strided(q, k, v, mask_bias, pair_bias, out, lse, shape, nullptr, dtype, stream);
+}
+
+evo_status_t evo_attn_fwd_strided(const void* q, const void* k, const void* v, const void* mask_bias,
+                                  const void* pair_bias, void* out, float* lse, const int64_t shape[5],
+                                  const int64_t strides[3], int dtype, void* stream) {
   Shape s;
   evo_status_t st = parse_shape(shape, dtype, &s);
   if (st != EVO_OK) return st;
+  Layout lay;
+  if ((st = parse_layout(s, strides, &lay)) != EVO_OK) return st;
   // lse may be NULL: a forward with no backward after it (inference)
   if (!q || !k || !v || !out) return EVO_ERR_NULL_POINTER;
   int dev = 0;
@@ -289,7 +343,7 @@ evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const voi
   const void* ptrs[] = {q, k, v, mask_bias, pair_bias, out, lse};
   for (const void* p : ptrs)
     if (p && (st = check_device_ptr(p, dev)) != EVO_OK) return st;
-  const int64_t tb = s.B * s.N * s.L * s.H * s.D * 2;
+  const int64_t tb = footprint_bytes(s, lay);
   const Range ins[] = {rng(q, tb), rng(k, tb), rng(v, tb), rng(mask_bias, s.B * s.N * s.L * 2),
                        rng(pair_bias, s.B * s.H * s.L * s.L * 2)};
   const Range outs[] = {rng(out, tb), rng(lse, s.B * s.N * s.H * s.L * 4)};
@@ -303,6 +357,9 @@ evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const voi
   a.pair = static_cast<const uint16_t*>(pair_bias);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
+  a.sB = lay.sB;
+  a.sN = lay.sN;
+  a.sL = lay.sL;
   a.B = (int)s.B;
   a.N = (int)s.N;
   a.L = (int)s.L;
@@ -336,9 +393,20 @@ evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const voi
                           const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
                           void* dmask_bias, void* dpair_bias, void* workspace, size_t workspace_bytes,
                           const int64_t shape[5], int dtype, void* stream) {
+  return evo_attn_bwd_strided(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias,
+                              workspace, workspace_bytes, shape, nullptr, dtype, stream);
+}
+
+evo_status_t evo_attn_bwd_strided(const void* q, const void* k, const void* v, const void* mask_bias,
+                                  const void* pair_bias, const void* out, const float* lse, const void* dout,
+                                  void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias, void* workspace,
+                                  size_t workspace_bytes, const int64_t shape[5], const int64_t strides[3],
+                                  int dtype, void* stream) {
   Shape s;
   evo_status_t st = parse_shape(shape, dtype, &s);
   if (st != EVO_OK) return st;
+  Layout lay;
+  if ((st = parse_layout(s, strides, &lay)) != EVO_OK) return st;
   if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return EVO_ERR_NULL_POINTER;
   if ((dmask_bias && !mask_bias) || (dpair_bias && !pair_bias)) return EVO_ERR_NULL_POINTER;
   const bool has_mask = mask_bias != nullptr, has_pair = pair_bias != nullptr;
@@ -350,7 +418,7 @@ evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const voi
   const void* ptrs[] = {q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias, workspace};
   for (const void* p : ptrs)
     if (p && (st = check_device_ptr(p, dev)) != EVO_OK) return st;
-  const int64_t tb = s.B * s.N * s.L * s.H * s.D * 2;
+  const int64_t tb = footprint_bytes(s, lay);
   const Range ins[] = {rng(q, tb),
                        rng(k, tb),
                        rng(v, tb),
@@ -388,6 +456,9 @@ evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const voi
   a.dpair_part = has_pair ? reinterpret_cast<float*>(ws + w.dpair_part) : nullptr;
   a.dpair_f32 = has_pair ? reinterpret_cast<float*>(ws + w.dpair_f32) : nullptr;
   a.dq_part = (w.dq_part != (size_t)-1) ? reinterpret_cast<float*>(ws + w.dq_part) : nullptr;
+  a.sB = lay.sB;
+  a.sN = lay.sN;
+  a.sL = lay.sL;
   a.B = (int)s.B;
   a.N = (int)s.N;
   a.L = (int)s.L;

@@ -35,7 +35,7 @@ namespace evo {
 //                                        consecutive elements each.
 template <class T, bool VEC>
 __global__ __launch_bounds__(256) void evo_bwd_fin_kernel(BwdArgs a, int ngroups, int64_t n_pair, int64_t n_mask,
-                                                          int64_t n_dq, int jtiles) {
+                                                          int64_t n_dq, int jtiles, int D) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e < n_pair) {
     const int64_t per = (int64_t)a.B * a.H * a.L * a.L;
@@ -86,7 +86,11 @@ __global__ __launch_bounds__(256) void evo_bwd_fin_kernel(BwdArgs a, int ngroups
     u32x2 w;
     w[0] = T::pack2(s[0], s[1]);
     w[1] = T::pack2(s[2], s[3]);
-    *reinterpret_cast<u32x2*>(a.dq + idx) = w;
+    // the partials are dense [B,N,L,H,D]; dQ has the strides of the call
+    const int64_t hd = idx % ((int64_t)a.H * D), r = idx / ((int64_t)a.H * D);
+    const int64_t l = r % a.L, bn = r / a.L;
+    const int64_t dst = (bn / a.N) * a.sB + (bn % a.N) * a.sN + l * a.sL + hd;
+    *reinterpret_cast<u32x2*>(a.dq + dst) = w;
   }
 }
 
@@ -117,10 +121,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     prof_begin(K_BWD_FIN, st);
     if (vec)
       hipLaunchKernelGGL((evo_bwd_fin_kernel<T, true>), dim3(blocks), dim3(256), 0, st, a, a.n_groups_q, n_pair,
-                         n_mask, n_dq, jtiles);
+                         n_mask, n_dq, jtiles, D);
     else
       hipLaunchKernelGGL((evo_bwd_fin_kernel<T, false>), dim3(blocks), dim3(256), 0, st, a, a.n_groups_q, n_pair,
-                         n_mask, n_dq, jtiles);
+                         n_mask, n_dq, jtiles, D);
     prof_end(K_BWD_FIN, st);
   }
   return hipGetLastError();

@@ -37,8 +37,9 @@ constexpr int kWaves = 8;
 
 // Per-thread byte offsets, relative to the first element of a (b, n) slice,
 // of the 16-byte chunks this thread copies into a tile (rows = keys
-// [kc0, kc0 + CH), clamped to L - 1; K-layout chunks first, then V-layout chunks).  They do not
-// depend on n, so the per-slice copy is a base pointer plus these offsets.
+// [kc0, kc0 + CH), clamped to L - 1, sL elements apart; K-layout chunks first,
+// then V-layout chunks).  They do not depend on n, so the per-slice copy is a
+// base pointer plus these offsets.
 template <int D, int NT>
 struct TileCopy {
   static constexpr int N = (KVTile<D>::TCH + NT - 1) / NT;  // chunks per thread (the last may be partial)
@@ -46,8 +47,8 @@ struct TileCopy {
 };
 
 template <int D, int NT>
-__device__ __forceinline__ void tile_chunk_offsets(TileCopy<D, NT>& tc, int kc0, int L, int H, int h, int wave,
-                                                   int lane) {
+__device__ __forceinline__ void tile_chunk_offsets(TileCopy<D, NT>& tc, int kc0, int L, int64_t sL, int h,
+                                                   int wave, int lane) {
   using TL = KVTile<D>;
 #pragma unroll
   for (int c = 0; c < TileCopy<D, NT>::N; ++c) {
@@ -63,7 +64,7 @@ __device__ __forceinline__ void tile_chunk_offsets(TileCopy<D, NT>& tc, int kc0,
       if (cc >= D / 8) cc = 0;  // columns the transposed reads touch but never use
     }
     const int j = min(kc0 + r, L - 1);
-    tc.off[c] = (uint32_t)((((size_t)j * H + h) * D + 8 * cc) * 2);
+    tc.off[c] = (uint32_t)((j * sL + h * D + 8 * cc) * 2);
   }
 }
 
@@ -157,22 +158,22 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   for (int e = 0; e < 4; ++e) ident[e] = (4 * g + e == col) ? T::one() : (short)0;
 
   TileCopy<D, NT> coff;
-  tile_chunk_offsets<D, NT>(coff, kc0, L, H, h, wave, lane);
+  tile_chunk_offsets<D, NT>(coff, kc0, L, a.sL, h, wave, lane);
 
   short8_t qop[KS32], gop[KS32], qnx[KS32], gnx[KS32], onx[KS32];
   float lse_nx = 0.f;
   uint32_t mraw = 0;
   const bool mask_thread = tid < TL::CH;
   auto load_rows = [&](int n) {
-    const size_t row = (((size_t)b * N + n) * L + ic) * H + h;
+    const int64_t row = b * a.sB + n * a.sN + ic * a.sL + h * D;  // element offset of the lane's row
 #pragma unroll
     for (int s = 0; s < KS32; ++s) {
       const int d0 = 32 * s + 8 * g;
       short8_t qv = {0, 0, 0, 0, 0, 0, 0, 0}, gv = qv, ov = qv;
       if (d0 + 8 <= D) {
-        qv = *reinterpret_cast<const short8_t*>(a.q + row * D + d0);
-        gv = *reinterpret_cast<const short8_t*>(a.dout + row * D + d0);
-        ov = *reinterpret_cast<const short8_t*>(a.out + row * D + d0);
+        qv = *reinterpret_cast<const short8_t*>(a.q + row + d0);
+        gv = *reinterpret_cast<const short8_t*>(a.dout + row + d0);
+        ov = *reinterpret_cast<const short8_t*>(a.out + row + d0);
       }
       qnx[s] = qv;
       gnx[s] = gv;
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   auto store_mask = [&](int buf) {
     if (mask_thread) smk[buf][tid] = (tid < lk) ? T::to_f32((uint16_t)mraw) * a.sqrt_d : kNegInf;
   };
-  auto slice_ptr = [&](const uint16_t* base, int n) { return base + ((size_t)b * N + n) * L * H * D; };
+  auto slice_ptr = [&](const uint16_t* base, int n) { return base + b * a.sB + n * a.sN; };
 
   floatx4 dpacc[WANT_DPAIR ? NB : 1];
 #pragma unroll
@@ -380,7 +381,8 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     });
     // ---- dQ = scale * dQ^T: lane holds d = 16 mb + 4 g + 0..3 of query i
     if (i_valid) {
-      const size_t row = (((size_t)b * N + n) * L + i) * H + h;
+      const size_t row = (((size_t)b * N + n) * L + i) * H + h;  // dense row index of the fp32 partials
+      const int64_t qoff = b * a.sB + n * a.sN + i * a.sL + h * D;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int d = 16 * mb + 4 * g;
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
             u32x2 w;
             w[0] = T::pack2(dq[mb][0] * scale, dq[mb][1] * scale);
             w[1] = T::pack2(dq[mb][2] * scale, dq[mb][3] * scale);
-            *reinterpret_cast<u32x2*>(a.dq + row * D + d) = w;
+            *reinterpret_cast<u32x2*>(a.dq + qoff + d) = w;
           }
         }
       }
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   }
 
   TileCopy<D, NT> coff;
-  tile_chunk_offsets<D, NT>(coff, 0, L, H, h, wave, lane);
+  tile_chunk_offsets<D, NT>(coff, 0, L, a.sL, h, wave, lane);
 
   // ---- per-slice key operands (B of S = Q K^T and dP = dO V^T): lane = key
   short8_t kop[KS32], vop[KS32], knx[KS32], vnx[KS32];
@@ -528,21 +530,21 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   float lse_nx = 0.f, del_nx = 0.f;
   const bool row_thread = tid < TL::CH;
   auto load_keys = [&](int n) {  // K, V rows and the mask of the lane's key
-    const size_t row = (((size_t)b * N + n) * L + jc) * H + h;
+    const int64_t row = b * a.sB + n * a.sN + jc * a.sL + h * D;
 #pragma unroll
     for (int s = 0; s < KS32; ++s) {
       const int d0 = 32 * s + 8 * g;
       short8_t kv = {0, 0, 0, 0, 0, 0, 0, 0}, vv = kv;
       if (d0 + 8 <= D) {
-        kv = *reinterpret_cast<const short8_t*>(a.k + row * D + d0);
-        vv = *reinterpret_cast<const short8_t*>(a.v + row * D + d0);
+        kv = *reinterpret_cast<const short8_t*>(a.k + row + d0);
+        vv = *reinterpret_cast<const short8_t*>(a.v + row + d0);
       }
       knx[s] = kv;
       vnx[s] = vv;
     }
     mnx = a.mask ? a.mask[((size_t)b * N + n) * L + jc] : 0u;
   };
-  auto slice_ptr = [&](const uint16_t* base, int n) { return base + ((size_t)b * N + n) * L * H * D; };
+  auto slice_ptr = [&](const uint16_t* base, int n) { return base + b * a.sB + n * a.sN; };
   int q0_nx = 0;
   auto load_rows = [&](int n, int q0) {  // lse, delta of query q0 + tid
     q0_nx = q0;
@@ -567,7 +569,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
     uint8_t* dst = smem + buf * TL::BUF_BYTES;
     if constexpr (MULTI) {
       TileCopy<D, NT> tc;
-      tile_chunk_offsets<D, NT>(tc, q0, L, H, h, wave, lane);
+      tile_chunk_offsets<D, NT>(tc, q0, L, a.sL, h, wave, lane);
       issue_tile<D, NT>(dst, qs, os, tc, wave);
     } else {
       issue_tile<D, NT>(dst, qs, os, coff, wave);
@@ -760,7 +762,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
     });
     // ---- dK = scale * dK^T, dV: lane holds d = 16 mb + 4 g + 0..3 of key j
     if (j_valid && qt == qtiles - 1) {
-      const size_t row = (((size_t)b * N + n) * L + j) * H + h;
+      const int64_t row = b * a.sB + n * a.sN + j * a.sL + h * D;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int d = 16 * mb + 4 * g;
@@ -770,8 +772,8 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
           wk[1] = T::pack2(dk[mb][2] * scale, dk[mb][3] * scale);
           wv[0] = T::pack2(dv[mb][0], dv[mb][1]);
           wv[1] = T::pack2(dv[mb][2], dv[mb][3]);
-          *reinterpret_cast<u32x2*>(a.dk + row * D + d) = wk;
-          *reinterpret_cast<u32x2*>(a.dv + row * D + d) = wv;
+          *reinterpret_cast<u32x2*>(a.dk + row + d) = wk;
+          *reinterpret_cast<u32x2*>(a.dv + row + d) = wv;
         }
       }
       if (WANT_DMASK && g == 0) a.dmask_part[(((size_t)b * N + n) * H + h) * L + j] = dmk[0];

@@ -218,34 +218,6 @@ struct KVTile {
   static_assert(TCH % 256 == 0, "tile must split evenly over 256 threads");
 };
 
-// Issue the asynchronous copy of keys [kc0, kc0 + CH) of one (b, n, h) slice
-// (K rows then V rows, swizzled) into an LDS tile buffer.  Every thread of a
-// 256-thread workgroup takes part; keys past L copy key L-1 (never used).
-template <int D>
-__device__ __forceinline__ void issue_kv_tile(uint8_t* buf, const uint16_t* k, const uint16_t* v, size_t slice_row,
-                                              int kc0, int L, int H, int h, int wave, int lane) {
-  using TL = KVTile<D>;
-  for (int base = wave * 64; base < TL::TCH; base += 256) {
-    const int q = base + lane;
-    const uint16_t* src;
-    if (q < TL::KCH) {
-      const int r = q / TL::KC, pos = q % TL::KC;
-      const int c = pos ^ kv_swz<TL::KC>(r);
-      const int j = min(kc0 + r, L - 1);
-      src = k + ((slice_row + j) * H + h) * D + 8 * c;
-    } else {
-      const int q2 = q - TL::KCH;
-      const int r = q2 / TL::VC, pos = q2 % TL::VC;
-      int c = pos ^ kv_swz<TL::VC>(r);
-      if (c >= D / 8) c = 0;  // columns the transposed reads touch but never use
-      const int j = min(kc0 + r, L - 1);
-      src = v + ((slice_row + j) * H + h) * D + 8 * c;
-    }
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)(buf + base * 16), 16, 0, 0);
-  }
-}
-
 // byte offset of element (row, col) in a swizzled tile with C chunks per row
 template <int C>
 __device__ __forceinline__ int tr_off(int row, int col) {

@@ -151,8 +151,7 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   uint32_t mraw = 0;  // this thread's mask value for the next tile (thread < CH)
 
   auto load_q = [&](short8_t (&dst)[S::KSTEPS_D], int n) {
-    const size_t slice = ((size_t)b * N + n) * L;
-    const uint16_t* qrow = a.q + ((slice + ic) * H + h) * D;
+    const uint16_t* qrow = a.q + b * a.sB + n * a.sN + ic * a.sL + h * D;
 #pragma unroll
     for (int s = 0; s < S::KSTEPS_D; ++s) {
       const int c = 16 * s + 8 * half;
@@ -180,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   auto issue_tile = [&](int t) {
     const int n = n_begin + t / nchunks;
     const int kc0 = (t % nchunks) * TL::CH;
-    const size_t slice = ((size_t)b * N + n) * L;
+    const int64_t slice = b * a.sB + n * a.sN + h * D;  // element offset of key 0's head h
     uint8_t* buf = smem + (t & 1) * TL::BUF_BYTES;
     for (int base = wave * 64; base < TL::TCH; base += 256) {
       const int q = base + lane;
@@ -189,14 +188,14 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
         const int r = q / TL::KC, pos = q % TL::KC;
         const int c = pos ^ kv_swz<TL::KC>(r);
         const int j = min(kc0 + r, L - 1);
-        src = a.k + ((slice + j) * H + h) * D + 8 * c;
+        src = a.k + slice + j * a.sL + 8 * c;
       } else {
         const int q2 = q - TL::KCH;
         const int r = q2 / TL::VC, pos = q2 % TL::VC;
         int c = pos ^ kv_swz<TL::VC>(r);
         if (c >= D / 8) c = 0;  // columns the transposed reads touch but never use
         const int j = min(kc0 + r, L - 1);
-        src = a.v + ((slice + j) * H + h) * D + 8 * c;
+        src = a.v + slice + j * a.sL + 8 * c;
       }
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(buf + base * 16), 16, 0, 0);
@@ -410,14 +409,13 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
     }
     if (c == nchunks - 1) {
       // ---- epilogue of slice n: normalise, store O and lse
-      const size_t slice = ((size_t)b * N + n) * L;
       const float l_tot = xhalf_sum(l_part);
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       {
         // lanes l and l^32 hold alternating runs of 4 columns of the same row;
         // one exchange per pair of runs gives each lane 8 contiguous columns,
         // stored as one 16-byte write
-        uint16_t* orow = a.out + ((slice + ic) * H + h) * D;
+        uint16_t* orow = a.out + b * a.sB + n * a.sN + ic * a.sL + h * D;
 #pragma unroll
         for (int mb2 = 0; mb2 < S::MB; ++mb2)
 #pragma unroll

@@ -13,7 +13,10 @@ struct FwdArgs {
   const uint16_t* mask;  // [B,N,L] or null
   const uint16_t* pair;  // [B,H,L,L] or null
   uint16_t* out;
-  float* lse;            // [B,N,H,L]
+  float* lse;            // [B,N,H,L] or null (nothing kept for a backward)
+  // element strides of dims B, N, L shared by q, k, v and out; the H heads of
+  // D elements of one (b, n, l) row are dense
+  int64_t sB, sN, sL;
   int B, N, L, H;
   int G;         // slices n per workgroup
   int n_groups;  // ceil(N / G)
@@ -41,7 +44,10 @@ struct BwdArgs {
   float* dmask_f32;      // [B,N,L]
   float* dpair_part;     // [n_groups_q, B, H, L, L] (when dpair requested)
   float* dpair_f32;      // [B,H,L,L]
-  float* dq_part;        // [jtiles, B,N,L,H,D] fp32 partials of dQ (rows longer than one key tile)
+  float* dq_part;        // [jtiles, B,N,L,H,D] fp32 partials of dQ (rows longer than one key tile), dense
+  // element strides of dims B, N, L shared by q, k, v, out, dout, dq, dk and
+  // dv; the H heads of D elements of one (b, n, l) row are dense
+  int64_t sB, sN, sL;
   int B, N, L, H;
   int Gq;          // slices per bwd_q3 workgroup
   int n_groups_q;

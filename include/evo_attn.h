@@ -21,7 +21,8 @@
  * Conventions common to every entry point
  *   - shape = {B, N, L, H, D}; B, N, L, H >= 1; D in {8, 16, 32, 64}.
  *   - Every tensor pointer is a DEVICE pointer on the current HIP device, to
- *     a dense row-major buffer, 16-byte aligned.  16-bit tensors hold IEEE
+ *     a dense row-major buffer, 16-byte aligned (the _strided entry points
+ *     take other layouts for the [B,N,L,H,D] tensors).  16-bit tensors hold IEEE
  *     half (EVO_F16) or bfloat16 (EVO_BF16) values; lse is float32.
  *   - All buffers are owned by the caller.  The library allocates no device
  *     memory and keeps no state between calls; calls are re-entrant.
@@ -58,7 +59,8 @@ typedef enum {
   EVO_ERR_WORKSPACE = 7,         /* workspace NULL or smaller than evo_attn_bwd_workspace_bytes() */
   EVO_ERR_DEVICE = 8,            /* the current device is not gfx950 */
   EVO_ERR_LAUNCH = 9,            /* a kernel launch failed */
-  EVO_ERR_ALIAS = 10             /* an output overlaps an input or another output */
+  EVO_ERR_ALIAS = 10,            /* an output overlaps an input or another output */
+  EVO_ERR_BAD_STRIDES = 11       /* strides not multiples of 8, rows that overlap, or a slice past 2 GiB */
 } evo_status_t;
 
 /* Forward (guide §3.5 and §3.7: fused attention that keeps O and the fp32 lse).
@@ -107,6 +109,30 @@ evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const voi
                           void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias,
                           void* workspace, size_t workspace_bytes, const int64_t shape[5], int dtype,
                           void* stream);
+
+/* The same operations on [B,N,L,H,D] tensors laid out with element strides
+ * strides = {sB, sN, sL} for dims B, N, L, shared by every such tensor of the
+ * call (q, k, v, out; and dout, dq, dk, dv for the backward); within one
+ * (b, n, l) row the H heads of D elements are dense.  Guide §3.6 names triangle
+ * attention around the ending node beside the starting-node form it shows:
+ * with sN and sL exchanged it runs on a view of the pair representation
+ * transposed over its two residue axes, without a copy.  Requirements (else
+ * EVO_ERR_BAD_STRIDES, before any device call): every stride a positive
+ * multiple of 8 elements; no two rows overlap (over the dims of extent > 1 in
+ * increasing stride order, each stride at least the span of the ones below
+ * it, the first at least H * D); (L - 1) * sL + H * D elements of one slice
+ * under 2 GiB.  strides == NULL is the dense layout {N*L*H*D, L*H*D, H*D}:
+ * evo_attn_fwd and evo_attn_bwd are these calls with NULL strides.  mask_bias,
+ * pair_bias, lse, their gradients and the workspace keep their dense layouts.
+ * Output values do not depend on the strides (bit for bit). */
+evo_status_t evo_attn_fwd_strided(const void* q, const void* k, const void* v, const void* mask_bias,
+                                  const void* pair_bias, void* out, float* lse, const int64_t shape[5],
+                                  const int64_t strides[3], int dtype, void* stream);
+evo_status_t evo_attn_bwd_strided(const void* q, const void* k, const void* v, const void* mask_bias,
+                                  const void* pair_bias, const void* out, const float* lse, const void* dout,
+                                  void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias,
+                                  void* workspace, size_t workspace_bytes, const int64_t shape[5],
+                                  const int64_t strides[3], int dtype, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* evo_status_string(int status);

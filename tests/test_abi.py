@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(0, 11):
+    for s in range(0, 12):
         assert _lib.evo_status_string(s)
     assert _lib.evo_status_string(99) == "unknown status"
 
@@ -60,3 +60,25 @@ def test_workspace_size_and_layout_host_logic():
     assert op + 1 * 2 * 32 * 32 * 4 <= full
     od, om, op = _lib.evo_attn_bwd_workspace_offsets(shape, 0, 0, 0)
     assert om is None and op is None
+
+
+@pytest.mark.parametrize("strides,code", [
+    ((8, 8, 7), 11),          # not a multiple of 8 elements
+    ((0, 64, 16), 11),        # not positive
+    ((1024, 64, 8), 11),      # L rows overlap: sL < H * D
+    ((1024, 32, 16), 11),     # N rows overlap the span of the L rows
+    ((2048, 16, 32), 1),      # transposed over N and L: valid (then the NULL pointers)
+    ((2048, 1024, 32), 1),    # padded rows: valid
+])
+def test_layout_errors_are_reported_before_any_device_call(strides, code):
+    shape = (2, 2, 32, 2, 8)  # H * D = 16
+    assert _lib.evo_attn_fwd_strided(None, None, None, None, None, None, None, shape, strides, 0, None) == code
+    assert _lib.evo_attn_bwd_strided(*([None] * 14), 0, shape, strides, 0, None) == code
+
+
+def test_layout_slice_limit():
+    # (L - 1) * sL + H * D elements of one slice must stay under 2 GiB
+    shape = (1, 1, 65536, 1, 8)
+    ok, bad = (1 << 40, 1 << 40, 16384), (1 << 40, 1 << 40, 16392)
+    assert _lib.evo_attn_fwd_strided(None, None, None, None, None, None, None, shape, ok, 0, None) == 1
+    assert _lib.evo_attn_fwd_strided(None, None, None, None, None, None, None, shape, bad, 0, None) == 11
