@@ -52,7 +52,7 @@ def parse():
 
 def kernel_sources_sha():
     h = hashlib.sha256()
-    for f in ("evo_common.h", "evo_fwd.hip", "evo_bwd.hip", "evo_api.hip", "evo_kernels.h"):
+    for f in ("evo_common.h", "evo_fwd.hip", "evo_bwd.hip", "evo_bwd_tile.hip", "evo_api.hip", "evo_kernels.h"):
         with open(os.path.join(ROOT, "evoformer_biased_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
