@@ -272,6 +272,25 @@ def main():
     del qt, kt, vt, dot, out_t, lse_t
     ms_bwd = timed_graph(lambda: attn_bwd(q, k, v, m, p, out, lse, do, workspace=ws))
 
+    # ---- padded batches of the same shape and score count (fp16 -inf masks past
+    # each entry's length): the kernels skip the 32-key blocks whose keys are all masked
+    def padded(pcfg):
+        pbits = I.make_inputs(pcfg)
+        pq, pk, pv, pm, pp, pdo = (dev_t(pbits[n]) for n in ("q", "k", "v", "mask_bias", "pair_bias", "dout"))
+        pws = attn_bwd(pq, pk, pv, pm, pp, *attn_fwd(pq, pk, pv, pm, pp), pdo)["workspace"]
+        ms_f = timed_graph(lambda: attn_fwd(pq, pk, pv, pm, pp))
+        ms_s = timed_graph(lambda: attn_bwd(pq, pk, pv, pm, pp, *attn_fwd(pq, pk, pv, pm, pp), pdo, workspace=pws))
+        pmask = I.as_float64(pbits, pcfg.dtype)["mask_bias"][:, :, 0, 0, :]
+        live = float((~np.isneginf(pmask).reshape(pcfg.B, pcfg.N, -1, 32).all(-1)).mean())
+        return {"ms": round(ms_s, 5), "fwd_ms": round(ms_f, 5), "live_block_fraction": round(live, 4),
+                "speedup_vs_unpadded": round(ms_step / ms_s, 3), "fwd_speedup_vs_unpadded": round(ms_fwd / ms_f, 3),
+                "workload": f"{pcfg.name}: Q,K,V {list(pcfg.shape)} {pcfg.dtype}, key lengths "
+                            f"{list(pcfg.key_lengths)} of {pcfg.L}, mask p={pcfg.mask_p}, seed {pcfg.seed}",
+                "note": "fwd+bwd step; 32-key blocks whose keys are all -inf are skipped"}
+
+    pad_uniform = padded(I.PADDED_UNIFORM)
+    pad_mixed = padded(I.PADDED)
+
     # ---- per-kernel launch times: HIP events the library records on this
     # stream around each of its kernels, over K more eager steps
     _lib.evo_attn_profile_read()
@@ -364,6 +383,8 @@ def main():
                           "note": "forward with no lse kept (no backward follows)"},
         "step_transposed_layout": {"ms": round(ms_step_t, 5), "tflops": round(tf_step * ms_step / ms_step_t, 2),
                                    "note": "fwd+bwd on Q, K, V, dO views transposed over N and L (no copy)"},
+        "padded_batch_uniform": pad_uniform,
+        "padded_batch_mixed": pad_mixed,
         "bwd": {"ms": round(ms_bwd, 5), "tflops": round(tf_bwd, 2), "pct_peak": round(100 * tf_bwd / PEAK_MFMA_TFLOPS, 2)},
         "kernels": {n: {"avg_us": round(v_["avg_us"], 2), "launches": v_["launches"], "share": round(v_["share"], 3)}
                     for n, v_ in kernels.items()},

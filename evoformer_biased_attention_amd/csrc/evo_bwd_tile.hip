@@ -1,5 +1,6 @@
-// Backward of Evoformer biased attention for rows that fit one key tile
-// (L <= 256, or L <= 128 at D = 64), gfx950.
+// Backward of Evoformer biased attention, gfx950: the query-side and key-side
+// tile kernels (rows of one key tile, L <= 256 or L <= 128 at D = 64, and,
+// with SPLIT / MULTI, longer rows).
 //
 // DeepSpeed4Science guide §3.7: recompute P from the saved fp32 lse, derive
 // delta = rowsum(dO * O), then dQ, dK, dV and the two bias gradients, the bias
@@ -21,7 +22,10 @@
 //     -inf for keys past L), so it costs neither a VALU op nor an MFMA;
 //   - -delta enters the dP MFMA the same way, so dS = P * acc is one multiply;
 //   - the n-sum of dpair is an MFMA against an identity operand;
-//   - LDS operand reads use the instruction's immediate offset field.
+//   - LDS operand reads use the instruction's immediate offset field;
+//   - keys masked with -inf have P = dS = 0: a 32-key step whose keys all are
+//     (bwd_q3) skips its vector work and its dQ and dpair products, and a wave
+//     whose 16 keys all are (bwd_kv3) skips the slice and writes zeros.
 // Per score the vector ALU then does: the bias add (fused with the scale),
 // the exp argument, the exp, dS = P * acc and a share of the 16-bit packing.
 #include "evo_common.h"
@@ -105,6 +109,9 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   constexpr int NT = 64 * NW, kRows = 16 * NW;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BUF_BYTES];
   __shared__ __attribute__((aligned(16))) float smk[2][TL::CH];  // sqrt(D) * mask of key j, -inf past L
+  // per slice, one byte per 32-key step: 1 when every key of the step is -inf
+  // (masked with -inf, or past L); such a step adds nothing to dQ or dpair
+  __shared__ __attribute__((aligned(8))) uint8_t sdead[2][8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -183,7 +190,15 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     if (mask_thread) mraw = a.mask ? a.mask[((size_t)b * N + n) * L + min(kc0 + tid, L - 1)] : 0u;
   };
   auto store_mask = [&](int buf) {
-    if (mask_thread) smk[buf][tid] = (tid < lk) ? T::to_f32((uint16_t)mraw) * a.sqrt_d : kNegInf;
+    if (mask_thread) {  // whole waves: CH is a multiple of 64
+      const float mv = (tid < lk) ? T::to_f32((uint16_t)mraw) * a.sqrt_d : kNegInf;
+      smk[buf][tid] = mv;
+      const uint64_t dead = __builtin_amdgcn_ballot_w64(mv == kNegInf);
+      if (lane == 0) {
+        sdead[buf][2 * wave] = (uint32_t)dead == ~0u;
+        sdead[buf][2 * wave + 1] = (uint32_t)(dead >> 32) == ~0u;
+      }
+    }
   };
   auto slice_ptr = [&](const uint16_t* base, int n) { return base + b * a.sB + n * a.sN; };
 
@@ -245,6 +260,10 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     const uint8_t* kb = smem + (t & 1) * TL::BUF_BYTES;
     const uint8_t* vb = kb + TL::KCH * 16;
     const float* mkb = &smk[t & 1][4 * g];
+    // dead-step bytes of this slice, wave-uniform
+    const u32x2 dw = *reinterpret_cast<const u32x2*>(&sdead[t & 1][0]);
+    const uint32_t dead_lo = __builtin_amdgcn_readfirstlane(dw[0]);
+    const uint32_t dead_hi = __builtin_amdgcn_readfirstlane(NSTEP > 4 ? dw[1] : 0u);
     // Row (key) 16 blk + col of a tile: the swizzle depends on col only, so a
     // block's operands sit at a fixed offset from the lane's base address.
     // For D < 32 the k-slots past D read finite tile data that meets zeros in
@@ -339,7 +358,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
           store_dpair(2 * st - 1);
         }
       }
-      if (32 * st < lk) {
+      if (32 * st < lk && (((st < 4 ? dead_lo : dead_hi) >> (8 * (st & 3))) & 0xffu) == 0u) {
         short4_t kt[2 * MB];  // [mb][lo/hi 16 keys]
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -577,7 +596,14 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   };
 
   floatx4 mk4 = {0.f, 0.f, 0.f, 0.f};
+  bool kdead = false;  // every key of this wave is -inf in the current slice: dK = dV = dmask = 0
   floatx4 dk[MB], dv[MB], dmk = {0.f, 0.f, 0.f, 0.f};
+  // bf16: the dmask column sums add the fp32 dS (a bf16-rounded dS, 2^-9
+  // relative, summed over H x L terms reaches the gradient tolerance when a
+  // row's probability sits on few keys); fp16 rounds 8x finer and keeps the
+  // column-sum MFMA
+  constexpr bool kDmaskF32 = std::is_same<T, BF16>::value;
+  float dmsum = 0.f;
   if (nu > 0) {
     load_keys(n_begin);
     load_rows(n_begin, 0);
@@ -602,12 +628,14 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
       // sqrt(D) * mask of the lane's key as the score accumulator input
       const float mk = j_valid ? T::to_f32((uint16_t)mnx) * a.sqrt_d : kNegInf;
       mk4 = floatx4{mk, mk, mk, mk};
+      kdead = __builtin_amdgcn_ballot_w64(mk == kNegInf) == ~0ull;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         dk[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
         dv[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
       dmk = floatx4{0.f, 0.f, 0.f, 0.f};
+      dmsum = 0.f;
     }
     if constexpr (MULTI && HAS_PAIR) {
       // this tile's bias columns; the slab is then free for the next tile's
@@ -696,71 +724,86 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
       }
     };
 
-    floatx4 sc[2][2], dp[2][2];
-    StepOps ops;
-    load_ops(std::integral_constant<int, 0>{}, ops);
-    lgkm_wait<0>();
-    touch_ops(ops, 0);
-    products(ops, sc[0], dp[0]);
-    if constexpr (NSTEP > 1) load_ops(std::integral_constant<int, 1>{}, ops);
-    static_for<0, NSTEP>([&](auto stc) {
-      constexpr int st = decltype(stc)::value;
-      constexpr int cur = st & 1;
-      if constexpr (st + 1 < NSTEP) {
-        lgkm_wait<0>();
-        touch_ops(ops, (st + 1) % 3);
-        products(ops, sc[cur ^ 1], dp[cur ^ 1]);
-        if constexpr (st + 2 < NSTEP) load_ops(std::integral_constant<int, st + 2>{}, ops);
-      }
-      if (32 * st < lq) {
-        short4_t tt[4 * MB];  // [mb][q lo, q hi, o lo, o hi]
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          tt[4 * mb + 0] = lds_tr_imm<st * 32 * KC * 16>(qtaddr[mb]);
-          tt[4 * mb + 1] = lds_tr_imm<st * 32 * KC * 16 + 16 * KC * 16>(qtaddr[mb]);
-          tt[4 * mb + 2] = lds_tr_imm<st * 32 * VC * 16>(otaddr[mb]);
-          tt[4 * mb + 3] = lds_tr_imm<st * 32 * VC * 16 + 16 * VC * 16>(otaddr[mb]);
+    if (!kdead) {
+      floatx4 sc[2][2], dp[2][2];
+      StepOps ops;
+      load_ops(std::integral_constant<int, 0>{}, ops);
+      lgkm_wait<0>();
+      touch_ops(ops, 0);
+      products(ops, sc[0], dp[0]);
+      if constexpr (NSTEP > 1) load_ops(std::integral_constant<int, 1>{}, ops);
+      static_for<0, NSTEP>([&](auto stc) {
+        constexpr int st = decltype(stc)::value;
+        constexpr int cur = st & 1;
+        if constexpr (st + 1 < NSTEP) {
+          lgkm_wait<0>();
+          touch_ops(ops, (st + 1) % 3);
+          products(ops, sc[cur ^ 1], dp[cur ^ 1]);
+          if constexpr (st + 2 < NSTEP) load_ops(std::integral_constant<int, st + 2>{}, ops);
         }
-        // keep the vector work below the reads so that it covers their latency
-        __builtin_amdgcn_sched_barrier(0);
-        float pv[2][4], ds[2][4];
+        if (32 * st < lq) {
+          short4_t tt[4 * MB];  // [mb][q lo, q hi, o lo, o hi]
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const int blk = 2 * st + hb;
-          const floatx4 nl4 = __builtin_bit_cast(floatx4, nlr[st % 3][hb]);
+          for (int mb = 0; mb < MB; ++mb) {
+            tt[4 * mb + 0] = lds_tr_imm<st * 32 * KC * 16>(qtaddr[mb]);
+            tt[4 * mb + 1] = lds_tr_imm<st * 32 * KC * 16 + 16 * KC * 16>(qtaddr[mb]);
+            tt[4 * mb + 2] = lds_tr_imm<st * 32 * VC * 16>(otaddr[mb]);
+            tt[4 * mb + 3] = lds_tr_imm<st * 32 * VC * 16 + 16 * VC * 16>(otaddr[mb]);
+          }
+          // keep the vector work below the reads so that it covers their latency
+          __builtin_amdgcn_sched_barrier(0);
+          float pv[2][4], ds[2][4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float x;
-            if constexpr (HAS_PAIR) {
-              const uint32_t w = pbias[blk][r / 2];
-              const float sv = (r & 1) ? T::fma_mix_hi(sc[cur][hb][r], scale, w) : T::fma_mix_lo(sc[cur][hb][r], scale, w);
-              x = __builtin_fmaf(sv, kLog2e, nl4[r]);
-            } else {
-              x = __builtin_fmaf(sc[cur][hb][r], c1, nl4[r]);
+          for (int hb = 0; hb < 2; ++hb) {
+            const int blk = 2 * st + hb;
+            const floatx4 nl4 = __builtin_bit_cast(floatx4, nlr[st % 3][hb]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float x;
+              if constexpr (HAS_PAIR) {
+                const uint32_t w = pbias[blk][r / 2];
+                const float sv = (r & 1) ? T::fma_mix_hi(sc[cur][hb][r], scale, w) : T::fma_mix_lo(sc[cur][hb][r], scale, w);
+                x = __builtin_fmaf(sv, kLog2e, nl4[r]);
+              } else {
+                x = __builtin_fmaf(sc[cur][hb][r], c1, nl4[r]);
+              }
+              const float p = __builtin_amdgcn_exp2f(x);
+              pv[hb][r] = p;
+              ds[hb][r] = p * dp[cur][hb][r];
             }
-            const float p = __builtin_amdgcn_exp2f(x);
-            pv[hb][r] = p;
-            ds[hb][r] = p * dp[cur][hb][r];
+          }
+          const short8_t pb = __builtin_bit_cast(
+              short8_t, u32x4{T::pack2(pv[0][0], pv[0][1]), T::pack2(pv[0][2], pv[0][3]), T::pack2(pv[1][0], pv[1][1]),
+                              T::pack2(pv[1][2], pv[1][3])});
+          const short8_t db = __builtin_bit_cast(
+              short8_t, u32x4{T::pack2(ds[0][0], ds[0][1]), T::pack2(ds[0][2], ds[0][3]), T::pack2(ds[1][0], ds[1][1]),
+                              T::pack2(ds[1][2], ds[1][3])});
+          if constexpr (WANT_DMASK) {
+            if constexpr (kDmaskF32) {
+              dmsum += ((ds[0][0] + ds[0][1]) + (ds[0][2] + ds[0][3])) + ((ds[1][0] + ds[1][1]) + (ds[1][2] + ds[1][3]));
+            } else {
+              dmk = T::mfma16(ones, db, dmk);
+            }
+          }
+          lgkm_wait<0>();
+#pragma unroll
+          for (int k = 0; k < 4 * MB; ++k) reg_touch(tt[k]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            dk[mb] = T::mfma16(cat4(tt[4 * mb], tt[4 * mb + 1]), db, dk[mb]);
+            dv[mb] = T::mfma16(cat4(tt[4 * mb + 2], tt[4 * mb + 3]), pb, dv[mb]);
           }
         }
-        const short8_t pb = __builtin_bit_cast(
-            short8_t, u32x4{T::pack2(pv[0][0], pv[0][1]), T::pack2(pv[0][2], pv[0][3]), T::pack2(pv[1][0], pv[1][1]),
-                            T::pack2(pv[1][2], pv[1][3])});
-        const short8_t db = __builtin_bit_cast(
-            short8_t, u32x4{T::pack2(ds[0][0], ds[0][1]), T::pack2(ds[0][2], ds[0][3]), T::pack2(ds[1][0], ds[1][1]),
-                            T::pack2(ds[1][2], ds[1][3])});
-        if constexpr (WANT_DMASK) dmk = T::mfma16(ones, db, dmk);
-        lgkm_wait<0>();
-#pragma unroll
-        for (int k = 0; k < 4 * MB; ++k) reg_touch(tt[k]);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          dk[mb] = T::mfma16(cat4(tt[4 * mb], tt[4 * mb + 1]), db, dk[mb]);
-          dv[mb] = T::mfma16(cat4(tt[4 * mb + 2], tt[4 * mb + 3]), pb, dv[mb]);
-        }
-      }
-    });
+      });
+    }  // !kdead
     // ---- dK = scale * dK^T, dV: lane holds d = 16 mb + 4 g + 0..3 of key j
+    if constexpr (WANT_DMASK && kDmaskF32) {
+      if (qt == qtiles - 1) {  // the four lane groups holding key j hold its partial sums
+        dmsum += __shfl_xor(dmsum, 16);
+        dmsum += __shfl_xor(dmsum, 32);
+        dmk[0] = dmsum;
+      }
+    }
     if (j_valid && qt == qtiles - 1) {
       const int64_t row = b * a.sB + n * a.sN + j * a.sL + h * D;
 #pragma unroll

@@ -22,6 +22,9 @@
 //   row of sqrt(D)*mask[j] (-inf for keys past L) sits in LDS, and each block
 //   starts its S^T accumulator from it, so the scale turns it back into
 //   mask[j] at no VALU or extra MFMA cost.
+//   Blocks of 32 keys whose mask is -inf throughout (padded keys) add nothing
+//   to a row (P = 0 there): per tile a byte per block records this, and such
+//   blocks skip the softmax, the V reads and the PV product.
 //   Running max: the exponent base is only moved when a row's block max
 //   exceeds it by more than 8 (log2 units), so exp values stay below 2^8 and
 //   the accumulator is rarely rescaled.
@@ -80,6 +83,9 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   constexpr int kSmem = 2 * TL::BUF_BYTES > kSlab ? 2 * TL::BUF_BYTES : kSlab;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   __shared__ __attribute__((aligned(16))) float smk[2][TL::CH];  // sqrt(D) * mask per key, -inf past L
+  // per tile, one byte per 32-key block: 1 when every key of the block is -inf
+  // (masked with -inf, or past L); such a block adds nothing and is skipped
+  __shared__ __attribute__((aligned(8))) uint8_t sdead[2][8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -172,7 +178,15 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   };
   auto store_mask = [&](int buf, int kc0) {
     if constexpr (HAS_MASK) {
-      if (tid < TL::CH) smk[buf][tid] = (kc0 + tid < L) ? T::to_f32((uint16_t)mraw) * a.sqrt_d : kNegInf;
+      if (tid < TL::CH) {  // whole waves: CH is a multiple of 64
+        const float mv = (kc0 + tid < L) ? T::to_f32((uint16_t)mraw) * a.sqrt_d : kNegInf;
+        smk[buf][tid] = mv;
+        const uint64_t dead = __builtin_amdgcn_ballot_w64(mv == kNegInf);
+        if (lane == 0) {
+          sdead[buf][2 * wave] = (uint32_t)dead == ~0u;
+          sdead[buf][2 * wave + 1] = (uint32_t)(dead >> 32) == ~0u;
+        }
+      }
     }
   };
   // issue the asynchronous copy of tile t into LDS buffer (t & 1)
@@ -264,7 +278,8 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
 
   // ---- bias, online softmax and O^T += V^T P^T for one block whose scores are in acc
   auto softmax_pv = [&](const floatx16& acc, const int tb, auto jbc, const u32x2 (&pb)[4],
-                        short8_t (&kpre)[S::KSTEPS_D], floatx16& mpre, auto prec, const bool pre_live) {
+                        short8_t (&kpre)[S::KSTEPS_D], floatx16& mpre, auto prec, const bool pre_live,
+                        const bool live) {
     constexpr int jb = decltype(jbc)::value, jb_pre = decltype(prec)::value;
     const uint32_t bufa = lds_addr(smem + tb * TL::BUF_BYTES);
     // V^T operands first: the reads complete under the softmax VALU work
@@ -274,6 +289,11 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
         k_fetch(prec, bufa, kpre);
         mc_fetch(tb, jb_pre, mpre);
       }
+    }
+    if (!live) {  // every score of the block is -inf: P = 0, nothing to add
+      short4_t none[2] = {};
+      lds_wait_all(none, kpre);
+      return;
     }
     short4_t vt[4 * S::MB];  // [t][mb][lo/hi]
     static_for<0, 2>([&](auto tc) {
@@ -371,6 +391,13 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
     // the QK^T MFMAs of block jb+1 run and the K operands and mask term of
     // block jb+2 load
     const int nblk = min(TL::CH, L - kc0 + 31) / 32;
+    // dead-block bytes of this tile, wave-uniform
+    uint32_t dead_lo = 0, dead_hi = 0;
+    if constexpr (HAS_MASK) {
+      const u32x2 dw = *reinterpret_cast<const u32x2*>(&sdead[tb][0]);
+      dead_lo = __builtin_amdgcn_readfirstlane(dw[0]);
+      dead_hi = __builtin_amdgcn_readfirstlane(TL::CH / 32 > 4 ? dw[1] : 0u);
+    }
     {
       constexpr int NB = (RES > 0 && RES < TL::CH / 32) ? RES : TL::CH / 32;
       short8_t kreg[2][S::KSTEPS_D];
@@ -397,12 +424,13 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
           // the K operands of block jb + 2 are read only when it exists
           const bool pre_live = jb + 2 < nblk;
           constexpr int jpre = jb + 2 < NB ? jb + 2 : -1;
+          const bool live = (((jb < 4 ? dead_lo : dead_hi) >> (8 * (jb & 3))) & 0xffu) == 0u;
           if constexpr (RES > 0) {
             softmax_pv(sacc[jb & 1], tb, jbc, pres[jb < RES ? jb : 0], kreg[jb & 1], mc,
-                       std::integral_constant<int, jpre>{}, pre_live);
+                       std::integral_constant<int, jpre>{}, pre_live, live);
           } else {
             softmax_pv(sacc[jb & 1], tb, jbc, ptile[HAS_PAIR ? jb : 0], kreg[jb & 1], mc,
-                       std::integral_constant<int, jpre>{}, pre_live);
+                       std::integral_constant<int, jpre>{}, pre_live, live);
           }
         }
       });

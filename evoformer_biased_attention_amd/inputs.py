@@ -18,14 +18,15 @@ own cast, bf16 by integer arithmetic on the float32 bit pattern.  -1e9 becomes
 Draw order for one call (all float32, one ``numpy.random.default_rng(seed)``):
 q, k, v ~ N(0,1); mask uniforms [B,N,L]; pair ~ N(0,1)*sigma (only when a
 pair bias is requested); dout ~ N(0,1).  A key is masked where its uniform is
-below ``mask_p``.  If every key of one (b, n) row would be masked, key 0 is
-left unmasked, so that no query row is fully masked.
+below ``mask_p`` or, for a padded batch, where it lies past its batch entry's
+length.  If every key of one (b, n) row would be masked, key 0 is left
+unmasked, so that no query row is fully masked.
 """
 from __future__ import annotations
 
 import dataclasses
 import hashlib
-from typing import Dict, Optional
+from typing import Dict, Optional, Tuple
 
 import numpy as np
 
@@ -48,6 +49,10 @@ class Config:
     mask_p: Optional[float] = 0.05  # None: no mask bias at all
     pair_sigma: Optional[float] = 1.0  # None: no pair bias at all
     seed: int = 0
+    # padded batch: keys j >= key_lengths[b] of every row of batch entry b are
+    # masked (as a padded residue or sequence axis is); None: no padding
+    key_lengths: Optional[Tuple[int, ...]] = None
+    mask_value: float = MASK_VALUE  # the additive bias of a masked key
 
     @property
     def shape(self):
@@ -136,9 +141,12 @@ def make_inputs(cfg: Config, seed: Optional[int] = None) -> Dict[str, Optional[n
     if cfg.mask_p is not None:
         u = rng.random((B, N, L), dtype=np.float32)
         masked = u < np.float32(cfg.mask_p)
+        if cfg.key_lengths is not None:
+            for b, n_keys in enumerate(cfg.key_lengths):
+                masked[b, :, n_keys:] = True
         full = masked.all(axis=-1)
         masked[full, 0] = False
-        mask = np.where(masked, np.float32(MASK_VALUE), np.float32(0.0)).astype(np.float32)
+        mask = np.where(masked, np.float32(cfg.mask_value), np.float32(0.0)).astype(np.float32)
         mask = mask.reshape(B, N, 1, 1, L)
     pair = None
     if cfg.pair_sigma is not None:
@@ -171,5 +179,19 @@ def digest(bits: Dict[str, Optional[np.ndarray]]) -> str:
 
 
 def custom(name: str, B: int, N: int, L: int, H: int, D: int, dtype: str = "fp16",
-           mask_p: Optional[float] = 0.1, pair_sigma: Optional[float] = 1.0, seed: int = 7) -> Config:
-    return Config(name, B, N, L, H, D, dtype, mask_p, pair_sigma, seed)
+           mask_p: Optional[float] = 0.1, pair_sigma: Optional[float] = 1.0, seed: int = 7,
+           key_lengths: Optional[Tuple[int, ...]] = None, mask_value: float = MASK_VALUE) -> Config:
+    if key_lengths is not None:
+        assert len(key_lengths) == B and all(1 <= n <= L for n in key_lengths), key_lengths
+    return Config(name, B, N, L, H, D, dtype, mask_p, pair_sigma, seed, key_lengths, mask_value)
+
+
+# Padded batches of the MSA-row shape (1,256,256,4,32) fp16, keys past a
+# length masked with -1e9 (which is -inf in fp16) on top of the 5% random key
+# mask, same score count as the unpadded workload:
+#  - uniform: one entry whose 160 residues are padded to 256 (62.5% of the
+#    32-key blocks hold a live key; the rest are skipped by the kernels);
+#  - mixed: four entries of 64 sequences with 256, 200, 160 and 96 residues
+#    padded to 256 (72% live blocks, unevenly spread over the workgroups).
+PADDED_UNIFORM = custom("msa_row_padded_uniform", 1, 256, 256, 4, 32, "fp16", 0.05, 1.0, 1013, key_lengths=(160,))
+PADDED = custom("msa_row_padded_mixed", 4, 64, 256, 4, 32, "fp16", 0.05, 1.0, 1012, key_lengths=(256, 200, 160, 96))

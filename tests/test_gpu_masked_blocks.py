@@ -1,0 +1,78 @@
+"""Blocks of keys masked with -inf: parity with the oracle where the kernels skip work.
+
+A key whose mask bias is -inf has P = 0 in every row, so it adds nothing to O,
+lse, dQ or dpair, and its dK, dV and dmask are zero.  The kernels skip a
+32-key block (forward, query-side backward) or a wave's 16 keys (key-side
+backward) when every key in it is -inf.  These cases put such blocks where
+the skip paths run: padded batches (fp16, where -1e9 overflows to -inf, and
+bf16 with an explicit -inf), interior dead blocks, a whole slice with every key
+masked (O = 0, lse = -inf, zero gradients), rows of one and of several key
+tiles, D = 16, 32 and 64, with and without the pair bias.  Tolerances and the
+comparison are those of the other parity tests.
+"""
+import numpy as np
+import pytest
+
+from evoformer_biased_attention_amd import inputs as I
+from tests.test_gpu_parity import _compare, _run_gpu
+
+pytestmark = pytest.mark.gpu
+
+NEG_INF = float("-inf")
+
+PADDED = [
+    I.custom("pad_l256_d32", 2, 6, 256, 4, 32, "fp16", 0.05, 1.0, 41, key_lengths=(256, 97)),
+    I.custom("pad_l200_d64", 2, 4, 200, 2, 64, "fp16", 0.05, 1.0, 42, key_lengths=(200, 50)),
+    I.custom("pad_l520_d16", 2, 2, 520, 1, 16, "fp16", 0.05, 1.0, 43, key_lengths=(300, 520)),
+    I.custom("pad_l384_bf16_inf_nopair", 2, 3, 384, 2, 32, "bf16", 0.05, None, 44, key_lengths=(384, 130),
+             mask_value=NEG_INF),
+    I.custom("pad_l256_bf16_inf", 2, 5, 256, 4, 32, "bf16", 0.05, 1.0, 45, key_lengths=(33, 256),
+             mask_value=NEG_INF),
+    I.custom("pad_l64_d8", 3, 4, 64, 2, 8, "fp16", 0.1, 1.0, 46, key_lengths=(64, 31, 1)),
+]
+
+
+@pytest.mark.parametrize("cfg", PADDED, ids=[c.name for c in PADDED])
+def test_parity_padded_batches(cfg):
+    print(f"case padded {cfg.name} shape={cfg.shape} dtype={cfg.dtype} lengths={cfg.key_lengths}", flush=True)
+    bits = I.make_inputs(cfg)
+    res = _run_gpu(cfg, bits)
+    _compare(cfg, bits, res)
+
+
+def _with_dead_blocks(cfg, blocks, dead_slices):
+    """Inputs of cfg with keys [lo, hi) of every row masked to -inf for each (lo, hi)
+    in blocks, and every key of the listed (b, n) slices masked to -inf."""
+    bits = I.make_inputs(cfg)
+    ninf = I.to_bits(np.array([NEG_INF], np.float32), cfg.dtype)[0]
+    m = bits["mask_bias"].copy()
+    for lo, hi in blocks:
+        m[..., lo:hi] = ninf
+    for b, n in dead_slices:
+        m[b, n] = ninf
+    bits["mask_bias"] = m
+    return bits
+
+
+DEAD = [
+    (I.custom("dead_l256_d32", 1, 6, 256, 4, 32, "fp16", 0.05, 1.0, 51), [(32, 64), (160, 224)], [(0, 2)]),
+    (I.custom("dead_l200_d64_bf16", 1, 4, 200, 2, 64, "bf16", 0.05, 1.0, 52), [(0, 32), (64, 128)], [(0, 3)]),
+    (I.custom("dead_l600_d32", 1, 3, 600, 2, 32, "fp16", 0.05, 1.0, 53), [(256, 512)], [(0, 1)]),
+    (I.custom("dead_l100_d16_nopair", 2, 3, 100, 2, 16, "fp16", 0.1, None, 54), [(0, 64)], [(1, 0)]),
+]
+
+
+@pytest.mark.parametrize("cfg,blocks,dead_slices", DEAD, ids=[c[0].name for c in DEAD])
+def test_parity_interior_dead_blocks(cfg, blocks, dead_slices):
+    print(f"case dead blocks {cfg.name} shape={cfg.shape} dtype={cfg.dtype} blocks={blocks} slices={dead_slices}",
+          flush=True)
+    bits = _with_dead_blocks(cfg, blocks, dead_slices)
+    res = _run_gpu(cfg, bits)
+    _compare(cfg, bits, res)
+    # a slice with every key masked: O = 0, lse = -inf, zero gradients, exactly
+    for b, n in dead_slices:
+        for key in ("out", "dq", "dk", "dv"):
+            assert not bool(res[key][b, n].any()), f"{key} of the fully masked slice is not zero"
+        assert bool(np.isneginf(res["lse"][b, n].cpu().numpy()).all()), "lse of the fully masked slice"
+        if res["dmask"] is not None:
+            assert not bool(res["dmask"][b, n].any()), "dmask of the fully masked slice is not zero"
