@@ -33,6 +33,30 @@ namespace evo {
 //   [n_pair + n_mask, ... + n_dq)        dQ = sum of the key-tile partials
 //                                        (rows longer than one key tile), 4
 //                                        consecutive elements each.
+// Sum of the n partials src[g * per] in a fixed order, with up to 16 loads in
+// flight per thread (the sum is bound by memory latency, not by the adds).
+template <class V>
+__device__ __forceinline__ V sum_partials(const V* src, int64_t per, int n) {
+  V acc[4] = {V{}, V{}, V{}, V{}};
+  int g = 0;
+  for (; g + 16 <= n; g += 16) {
+    V t[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) t[u] = src[(int64_t)(g + u) * per];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc[u & 3] += t[u];
+  }
+  for (; g + 4 <= n; g += 4) {
+    V t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t[u] = src[(int64_t)(g + u) * per];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += t[u];
+  }
+  for (; g < n; ++g) acc[0] += src[(int64_t)g * per];
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 template <class T, bool VEC>
 __global__ __launch_bounds__(256) void evo_bwd_fin_kernel(BwdArgs a, int ngroups, int64_t n_pair, int64_t n_mask,
                                                           int64_t n_dq, int jtiles, int D) {
@@ -41,28 +65,14 @@ __global__ __launch_bounds__(256) void evo_bwd_fin_kernel(BwdArgs a, int ngroups
     const int64_t per = (int64_t)a.B * a.H * a.L * a.L;
     if constexpr (VEC) {
       const int64_t idx = 4 * e;
-      floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
-      int gg = 0;
-      for (; gg + 1 < ngroups; gg += 2) {
-        s0 += *reinterpret_cast<const floatx4*>(a.dpair_part + (int64_t)gg * per + idx);
-        s1 += *reinterpret_cast<const floatx4*>(a.dpair_part + (int64_t)(gg + 1) * per + idx);
-      }
-      if (gg < ngroups) s0 += *reinterpret_cast<const floatx4*>(a.dpair_part + (int64_t)gg * per + idx);
-      const floatx4 s = s0 + s1;
+      const floatx4 s = sum_partials(reinterpret_cast<const floatx4*>(a.dpair_part) + e, per / 4, ngroups);
       *reinterpret_cast<floatx4*>(a.dpair_f32 + idx) = s;
       u32x2 w;
       w[0] = T::pack2(s[0], s[1]);
       w[1] = T::pack2(s[2], s[3]);
       *reinterpret_cast<u32x2*>(a.dpair + idx) = w;
     } else {
-      float s0 = 0.f, s1 = 0.f;
-      int gg = 0;
-      for (; gg + 1 < ngroups; gg += 2) {
-        s0 += a.dpair_part[(int64_t)gg * per + e];
-        s1 += a.dpair_part[(int64_t)(gg + 1) * per + e];
-      }
-      if (gg < ngroups) s0 += a.dpair_part[(int64_t)gg * per + e];
-      const float s = s0 + s1;
+      const float s = sum_partials(a.dpair_part + e, per, ngroups);
       a.dpair_f32[e] = s;
       a.dpair[e] = T::from_f32(s);
     }
@@ -72,8 +82,7 @@ __global__ __launch_bounds__(256) void evo_bwd_fin_kernel(BwdArgs a, int ngroups
   if (m < n_mask) {
     const int j = (int)(m % a.L);
     const int64_t bn = m / a.L;
-    float s = 0.f;
-    for (int hh = 0; hh < a.H; ++hh) s += a.dmask_part[(bn * a.H + hh) * a.L + j];
+    const float s = sum_partials(a.dmask_part + bn * a.H * a.L + j, (int64_t)a.L, a.H);
     a.dmask_f32[m] = s;
     a.dmask[m] = T::from_f32(s);
     return;
