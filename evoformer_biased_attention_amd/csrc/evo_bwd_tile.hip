@@ -221,38 +221,46 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     }
   };
 
-  if (ntiles > 0) {
-    load_rows(n_begin);
-    issue_tile<D, NT>(smem, slice_ptr(a.k, n_begin), slice_ptr(a.v, n_begin), coff, wave);
-    store_mask(0);
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    const int n = n_begin + t;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  // Q and dO rows of slice n into the operand registers, -lse log2e, and
+  // delta = rowsum(dO * O) (written for bwd_kv3 by the first key tile's
+  // workgroups) as the dP accumulator input -delta
+  float nl = 0.f;
+  floatx4 ndel = {0.f, 0.f, 0.f, 0.f};
+  auto take_rows = [&](int n) {
 #pragma unroll
     for (int s = 0; s < KS32; ++s) {
       qop[s] = qnx[s];
       gop[s] = gnx[s];
     }
-    const float nl = (lse_nx == kNegInf) ? kNegInf : -lse_nx * kLog2e;  // rows with no finite score: P = 0
-    float del;
-    {
-      // delta of this lane's query: dot over its 8 columns, then over the four
-      // lane groups that hold the same query
-      float part = 0.f;
+    nl = (lse_nx == kNegInf) ? kNegInf : -lse_nx * kLog2e;  // rows with no finite score: P = 0
+    // delta of this lane's query: dot over its 8 columns, then over the four
+    // lane groups that hold the same query
+    float part = 0.f;
 #pragma unroll
-      for (int s = 0; s < KS32; ++s) {
-        const u32x4 gw = __builtin_bit_cast(u32x4, gnx[s]), ow = __builtin_bit_cast(u32x4, onx[s]);
+    for (int s = 0; s < KS32; ++s) {
+      const u32x4 gw = __builtin_bit_cast(u32x4, gnx[s]), ow = __builtin_bit_cast(u32x4, onx[s]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part = T::dot2(gw[e], ow[e], part);
-      }
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      del = part;
-      if (g == 0 && i_valid && jt == 0) a.delta[(((size_t)b * N + n) * H + h) * L + i] = del;
+      for (int e = 0; e < 4; ++e) part = T::dot2(gw[e], ow[e], part);
     }
-    const floatx4 ndel = {-del, -del, -del, -del};
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if (g == 0 && i_valid && jt == 0) a.delta[(((size_t)b * N + n) * H + h) * L + i] = part;
+    ndel = floatx4{-part, -part, -part, -part};
+  };
+
+  if (ntiles > 0) {
+    load_rows(n_begin);
+    issue_tile<D, NT>(smem, slice_ptr(a.k, n_begin), slice_ptr(a.v, n_begin), coff, wave);
+    store_mask(0);
+    vm_wait_all();
+    take_rows(n_begin);
+  }
+  // The next slice's copies and row loads are completed, and its rows taken
+  // into the operand registers, before this slice's dQ stores are issued: no
+  // wait (the barrier's or the compiler's) then waits for those stores.
+  for (int t = 0; t < ntiles; ++t) {
+    const int n = n_begin + t;
+    lds_barrier();
     if (t + 1 < ntiles) {
       issue_tile<D, NT>(smem + ((t + 1) & 1) * TL::BUF_BYTES, slice_ptr(a.k, n + 1), slice_ptr(a.v, n + 1), coff, wave);
       load_rows(n + 1);
@@ -398,6 +406,11 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
         for (int mb = 0; mb < MB; ++mb) dq[mb] = T::mfma16(cat4(kt[2 * mb], kt[2 * mb + 1]), dsb, dq[mb]);
       }
     });
+    vm_wait_all();  // the next slice's copies and row loads
+    if (t + 1 < ntiles) {
+      store_mask((t + 1) & 1);  // its buffer was last read during slice t-1
+      take_rows(n + 1);
+    }
     // ---- dQ = scale * dQ^T: lane holds d = 16 mb + 4 g + 0..3 of query i
     if (i_valid) {
       const size_t row = (((size_t)b * N + n) * L + i) * H + h;  // dense row index of the fp32 partials
@@ -418,7 +431,6 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
         }
       }
     }
-    if (t + 1 < ntiles) store_mask((t + 1) & 1);
   }
 
   if constexpr (WANT_DPAIR) {
@@ -597,6 +609,18 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
 
   floatx4 mk4 = {0.f, 0.f, 0.f, 0.f};
   bool kdead = false;  // every key of this wave is -inf in the current slice: dK = dV = dmask = 0
+  // the slice's K and V rows of the lane's key into the operand registers, and
+  // sqrt(D) * mask of the key as the score accumulator input
+  auto take_keys = [&]() {
+#pragma unroll
+    for (int s = 0; s < KS32; ++s) {
+      kop[s] = knx[s];
+      vop[s] = vnx[s];
+    }
+    const float mk = j_valid ? T::to_f32((uint16_t)mnx) * a.sqrt_d : kNegInf;
+    mk4 = floatx4{mk, mk, mk, mk};
+    kdead = __builtin_amdgcn_ballot_w64(mk == kNegInf) == ~0ull;
+  };
   floatx4 dk[MB], dv[MB], dmk = {0.f, 0.f, 0.f, 0.f};
   // bf16: the dmask column sums add the fp32 dS (a bf16-rounded dS, 2^-9
   // relative, summed over H x L terms reaches the gradient tolerance when a
@@ -612,23 +636,18 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
       if ((L % 8) == 0) issue_slab(sslab, 0);
     }
     store_rows(0);
+    vm_wait_all();
+    take_keys();
   }
+  // The next step's copies and loads are completed, and its rows and keys
+  // taken, before this step's dK, dV stores are issued: no wait (a barrier's
+  // or the compiler's) then waits for those stores.
   for (int u = 0; u < nu; ++u) {
     const int t = u / qtiles, qt = u % qtiles, q0 = qt * TL::CH;
     const int n = n_begin + t;
     const int lq = L - q0;  // queries of the row from this tile on
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    lds_barrier();
     if (qt == 0) {
-#pragma unroll
-      for (int s = 0; s < KS32; ++s) {
-        kop[s] = knx[s];
-        vop[s] = vnx[s];
-      }
-      // sqrt(D) * mask of the lane's key as the score accumulator input
-      const float mk = j_valid ? T::to_f32((uint16_t)mnx) * a.sqrt_d : kNegInf;
-      mk4 = floatx4{mk, mk, mk, mk};
-      kdead = __builtin_amdgcn_ballot_w64(mk == kNegInf) == ~0ull;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         dk[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -641,7 +660,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
       // this tile's bias columns; the slab is then free for the next tile's
       if ((L % 8) == 0) {
         read_slab(sslab);
-        __syncthreads();
+        lds_barrier();
       } else {
         gather_bias(q0);
       }
@@ -796,6 +815,11 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
         }
       });
     }  // !kdead
+    vm_wait_all();  // the next step's copies and loads
+    if (u + 1 < nu) {
+      store_rows((u + 1) & 1);  // its buffers were last read during step u-1
+      if ((u + 1) % qtiles == 0) take_keys();
+    }
     // ---- dK = scale * dK^T, dV: lane holds d = 16 mb + 4 g + 0..3 of key j
     if constexpr (WANT_DMASK && kDmaskF32) {
       if (qt == qtiles - 1) {  // the four lane groups holding key j hold its partial sums
@@ -821,7 +845,6 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
       }
       if (WANT_DMASK && g == 0) a.dmask_part[(((size_t)b * N + n) * H + h) * L + j] = dmk[0];
     }
-    if (u + 1 < nu) store_rows((u + 1) & 1);
   }
 }
 

@@ -333,6 +333,32 @@ template <int N>
 __device__ __forceinline__ void lgkm_wait() {
   asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N) : "memory");
 }
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8; a field at its maximum does not wait).  Issued
+// through the builtin so that the compiler's own wait insertion knows what
+// has completed; the empty asm statements keep memory accesses on their side.
+constexpr unsigned kWaitVm0 = 0x0F70;    // vmcnt(0)
+constexpr unsigned kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
+
+// Wait until every vector memory operation of this thread has completed:
+// loads, asynchronous copies into LDS, and stores.
+__device__ __forceinline__ void vm_wait_all() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier for LDS: waits for this thread's LDS operations only, not
+// for its global stores still in flight (a __syncthreads() also waits for
+// those).  Callers complete their asynchronous LDS copies with vm_wait_all()
+// before it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Make a register value an output of an (empty) asm placed after a wait, so
 // that no use of it is scheduled before the wait.
 template <class R>

@@ -357,16 +357,19 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
     load_mask(n_begin, 0);
     load_q(qnext, n_begin);
     store_mask(0, 0);
+    vm_wait_all();
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS_D; ++s) qop[s] = qnext[s];
   }
+  // Tile t's copies (and its mask / Q loads) are completed by each thread
+  // before tile t-1's output stores are issued, so the barrier at the top of
+  // tile t waits for no store.
   for (int t = 0; t < ntiles; ++t) {
     const int n = n_begin + t / nchunks;
     const int c = t % nchunks;
     const int kc0 = c * TL::CH;
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's copies of tile t (and its mask/Q loads) are done
-    __syncthreads();                // everyone's are; everyone has finished tile t-1
+    lds_barrier();  // everyone's copies of tile t are done; everyone has finished tile t-1
     if (c == 0) {
-#pragma unroll
-      for (int s = 0; s < S::KSTEPS_D; ++s) qop[s] = qnext[s];
 #pragma unroll
       for (int mb2 = 0; mb2 < S::MB; ++mb2) oacc[mb2] = floatx16{};
       m_used = kNegInf;
@@ -435,6 +438,17 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
         }
       });
     }
+    // Tile t+1's copies and loads were issued a tile ago.  Its mask row and
+    // Q rows are taken now, before this tile's output stores are issued, so
+    // that no wait for them (the compiler's included) waits for those stores.
+    vm_wait_all();
+    if (t + 1 < ntiles) {
+      store_mask((t + 1) & 1, ((t + 1) % nchunks) * TL::CH);  // its buffer was last read during tile t-1
+      if ((t + 1) % nchunks == 0) {
+#pragma unroll
+        for (int s = 0; s < S::KSTEPS_D; ++s) qop[s] = qnext[s];
+      }
+    }
     if (c == nchunks - 1) {
       // ---- epilogue of slice n: normalise, store O and lse
       const float l_tot = xhalf_sum(l_part);
@@ -474,8 +488,6 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
         }
       }
     }
-    // the next tile's mask row (its buffer was last read during tile t - 1)
-    if (t + 1 < ntiles) store_mask((t + 1) & 1, ((t + 1) % nchunks) * TL::CH);
   }
 }
 
