@@ -358,14 +358,6 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
         products(ops, sc[cur ^ 1], dp[cur ^ 1]);
         if constexpr (st + 2 < NSTEP) load_ops(std::integral_constant<int, st + 2>{}, ops);
       }
-      // in the group's last slice, blocks are final once their step is done:
-      // their stores overlap the remaining steps
-      if constexpr (WANT_DPAIR && st >= 1) {
-        if (t + 1 == ntiles) {
-          store_dpair(2 * st - 2);
-          store_dpair(2 * st - 1);
-        }
-      }
       if (32 * st < lk && (((st < 4 ? dead_lo : dead_hi) >> (8 * (st & 3))) & 0xffu) == 0u) {
         short4_t kt[2 * MB];  // [mb][lo/hi 16 keys]
 #pragma unroll
@@ -435,8 +427,8 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
 
   if constexpr (WANT_DPAIR) {
     if (ntiles > 0) {
-      store_dpair(NB - 2);
-      store_dpair(NB - 1);
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) store_dpair(blk);
     }
   }
 }
