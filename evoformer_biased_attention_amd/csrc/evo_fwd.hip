@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   };
 
   floatx16 oacc[S::MB];
-  float m_used = kNegInf, l_part = 0.f;
+  float m_used = kNegInf, l_part = 0.f, l_part2 = 0.f;  // row sum in two chains
 
   // Per-lane byte offsets within a tile buffer.  The swizzle repeats every 16
   // rows, so block jb of a tile adds the constant 32 jb rows, which goes into
@@ -317,9 +317,12 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) sv[rr] = acc[rr] * a.scale;
     }
-    float mb = sv[0];
+    // block max as a tree of three-input maxima (depth 3, not 8)
+    float t5[5];
 #pragma unroll
-    for (int rr = 1; rr < 16; ++rr) mb = __builtin_fmaxf(mb, sv[rr]);
+    for (int q = 0; q < 5; ++q) t5[q] = __builtin_fmaxf(__builtin_fmaxf(sv[3 * q], sv[3 * q + 1]), sv[3 * q + 2]);
+    float mb = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(t5[0], t5[1]), t5[2]),
+                               __builtin_fmaxf(__builtin_fmaxf(t5[3], t5[4]), sv[15]));
     mb = xhalf_max(mb);
     const bool need = mb > m_used + kTauNat;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -327,6 +330,7 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       const float alpha = need ? __builtin_amdgcn_exp2f((m_used - m_new) * kLog2e) : 1.f;
       m_used = m_new;
       l_part *= alpha;
+      l_part2 *= alpha;
 #pragma unroll
       for (int mb2 = 0; mb2 < S::MB; ++mb2)
 #pragma unroll
@@ -339,7 +343,11 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr], kLog2e, neg_ml));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr + 1], kLog2e, neg_ml));
       pk[rr / 2] = T::pack2(p0, p1);
-      l_part = T::rowsum_add(l_part, p0, p1, pk[rr / 2]);
+      if ((rr / 2) & 1) {
+        l_part2 = T::rowsum_add(l_part2, p0, p1, pk[rr / 2]);
+      } else {
+        l_part = T::rowsum_add(l_part, p0, p1, pk[rr / 2]);
+      }
     }
     lds_wait_all(vt, kpre);
 #pragma unroll
@@ -374,6 +382,7 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       for (int mb2 = 0; mb2 < S::MB; ++mb2) oacc[mb2] = floatx16{};
       m_used = kNegInf;
       l_part = 0.f;
+      l_part2 = 0.f;
     }
     // streamed pair bias: this tile's blocks are loaded before the next tile's
     // copies are issued, so waiting for them never waits for the prefetch
@@ -451,7 +460,7 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
     }
     if (c == nchunks - 1) {
       // ---- epilogue of slice n: normalise, store O and lse
-      const float l_tot = xhalf_sum(l_part);
+      const float l_tot = xhalf_sum(l_part + l_part2);
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       {
         // lanes l and l^32 hold alternating runs of 4 columns of the same row;
