@@ -23,9 +23,10 @@
 //   - -delta enters the dP MFMA the same way, so dS = P * acc is one multiply;
 //   - the n-sum of dpair is an MFMA against an identity operand;
 //   - LDS operand reads use the instruction's immediate offset field;
-//   - keys masked with -inf have P = dS = 0: a 32-key step whose keys all are
-//     (bwd_q3) skips its vector work and its dQ and dpair products, and a wave
-//     whose 16 keys all are (bwd_kv3) skips the slice and writes zeros.
+//   - keys masked with -inf have P = dS = 0: bwd_q3 stops a slice's steps at
+//     the tile's last key that is not -inf (the padding at the end of a row
+//     is not computed), and a bwd_kv3 wave whose 16 keys all are -inf skips
+//     the slice and writes zeros.
 // Per score the vector ALU then does: the bias add (fused with the scale),
 // the exp argument, the exp, dS = P * acc and a share of the 16-bit packing.
 #include "evo_common.h"
@@ -109,9 +110,10 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   constexpr int NT = 64 * NW, kRows = 16 * NW;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BUF_BYTES];
   __shared__ __attribute__((aligned(16))) float smk[2][TL::CH];  // sqrt(D) * mask of key j, -inf past L
-  // per slice, one byte per 32-key step: 1 when every key of the step is -inf
-  // (masked with -inf, or past L); such a step adds nothing to dQ or dpair
-  __shared__ __attribute__((aligned(8))) uint8_t sdead[2][8];
+  // per slice and wave: 1 + the tile position of the wave's last key that is
+  // not -inf (masked with -inf, or past L), 0 if there is none; the keys past
+  // the largest add nothing to dQ or dpair
+  __shared__ __attribute__((aligned(16))) int slive[2][4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -193,11 +195,8 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     if (mask_thread) {  // whole waves: CH is a multiple of 64
       const float mv = (tid < lk) ? T::to_f32((uint16_t)mraw) * a.sqrt_d : kNegInf;
       smk[buf][tid] = mv;
-      const uint64_t dead = __builtin_amdgcn_ballot_w64(mv == kNegInf);
-      if (lane == 0) {
-        sdead[buf][2 * wave] = (uint32_t)dead == ~0u;
-        sdead[buf][2 * wave + 1] = (uint32_t)(dead >> 32) == ~0u;
-      }
+      const uint64_t live = __builtin_amdgcn_ballot_w64(mv != kNegInf);
+      if (lane == 0) slive[buf][wave] = live ? 64 * wave + 64 - (int)__builtin_clzll(live) : 0;
     }
   };
   auto slice_ptr = [&](const uint16_t* base, int n) { return base + b * a.sB + n * a.sN; };
@@ -268,10 +267,14 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     const uint8_t* kb = smem + (t & 1) * TL::BUF_BYTES;
     const uint8_t* vb = kb + TL::KCH * 16;
     const float* mkb = &smk[t & 1][4 * g];
-    // dead-step bytes of this slice, wave-uniform
-    const u32x2 dw = *reinterpret_cast<const u32x2*>(&sdead[t & 1][0]);
-    const uint32_t dead_lo = __builtin_amdgcn_readfirstlane(dw[0]);
-    const uint32_t dead_hi = __builtin_amdgcn_readfirstlane(NSTEP > 4 ? dw[1] : 0u);
+    // keys of the slice up to the tile's last key that is not -inf
+    int lkl;
+    {
+      const u32x4 lv = *reinterpret_cast<const u32x4*>(&slive[t & 1][0]);
+      const int le = TL::CH > 128 ? max(max((int)lv[0], (int)lv[1]), max((int)lv[2], (int)lv[3]))
+                                  : max((int)lv[0], (int)lv[1]);
+      lkl = min(lk, __builtin_amdgcn_readfirstlane(le));
+    }
     // Row (key) 16 blk + col of a tile: the swizzle depends on col only, so a
     // block's operands sit at a fixed offset from the lane's base address.
     // For D < 32 the k-slots past D read finite tile data that meets zeros in
@@ -358,7 +361,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
         products(ops, sc[cur ^ 1], dp[cur ^ 1]);
         if constexpr (st + 2 < NSTEP) load_ops(std::integral_constant<int, st + 2>{}, ops);
       }
-      if (32 * st < lk && (((st < 4 ? dead_lo : dead_hi) >> (8 * (st & 3))) & 0xffu) == 0u) {
+      if (32 * st < lkl) {
         short4_t kt[2 * MB];  // [mb][lo/hi 16 keys]
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {

@@ -22,9 +22,9 @@
 //   row of sqrt(D)*mask[j] (-inf for keys past L) sits in LDS, and each block
 //   starts its S^T accumulator from it, so the scale turns it back into
 //   mask[j] at no VALU or extra MFMA cost.
-//   Blocks of 32 keys whose mask is -inf throughout (padded keys) add nothing
-//   to a row (P = 0 there): per tile a byte per block records this, and such
-//   blocks skip the softmax, the V reads and the PV product.
+//   Keys masked with -inf add nothing to a row (P = 0 there).  Per tile the
+//   end of its last key that is not -inf is recorded, and the 32-key blocks
+//   past it (the padding at the end of a row) are not computed.
 //   Running max: the exponent base is only moved when a row's block max
 //   exceeds it by more than 8 (log2 units), so exp values stay below 2^8 and
 //   the accumulator is rarely rescaled.
@@ -83,9 +83,9 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   constexpr int kSmem = 2 * TL::BUF_BYTES > kSlab ? 2 * TL::BUF_BYTES : kSlab;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   __shared__ __attribute__((aligned(16))) float smk[2][TL::CH];  // sqrt(D) * mask per key, -inf past L
-  // per tile, one byte per 32-key block: 1 when every key of the block is -inf
-  // (masked with -inf, or past L); such a block adds nothing and is skipped
-  __shared__ __attribute__((aligned(8))) uint8_t sdead[2][8];
+  // per tile and wave: 1 + the tile position of the wave's last key that is
+  // not -inf (masked with -inf, or past L), 0 if there is none
+  __shared__ __attribute__((aligned(16))) int slive[2][4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -181,11 +181,8 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       if (tid < TL::CH) {  // whole waves: CH is a multiple of 64
         const float mv = (kc0 + tid < L) ? T::to_f32((uint16_t)mraw) * a.sqrt_d : kNegInf;
         smk[buf][tid] = mv;
-        const uint64_t dead = __builtin_amdgcn_ballot_w64(mv == kNegInf);
-        if (lane == 0) {
-          sdead[buf][2 * wave] = (uint32_t)dead == ~0u;
-          sdead[buf][2 * wave + 1] = (uint32_t)(dead >> 32) == ~0u;
-        }
+        const uint64_t live = __builtin_amdgcn_ballot_w64(mv != kNegInf);
+        if (lane == 0) slive[buf][wave] = live ? 64 * wave + 64 - (int)__builtin_clzll(live) : 0;
       }
     }
   };
@@ -278,8 +275,7 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
 
   // ---- bias, online softmax and O^T += V^T P^T for one block whose scores are in acc
   auto softmax_pv = [&](const floatx16& acc, const int tb, auto jbc, const u32x2 (&pb)[4],
-                        short8_t (&kpre)[S::KSTEPS_D], floatx16& mpre, auto prec, const bool pre_live,
-                        const bool live) {
+                        short8_t (&kpre)[S::KSTEPS_D], floatx16& mpre, auto prec, const bool pre_live) {
     constexpr int jb = decltype(jbc)::value, jb_pre = decltype(prec)::value;
     const uint32_t bufa = lds_addr(smem + tb * TL::BUF_BYTES);
     // V^T operands first: the reads complete under the softmax VALU work
@@ -289,11 +285,6 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
         k_fetch(prec, bufa, kpre);
         mc_fetch(tb, jb_pre, mpre);
       }
-    }
-    if (!live) {  // every score of the block is -inf: P = 0, nothing to add
-      short4_t none[2] = {};
-      lds_wait_all(none, kpre);
-      return;
     }
     short4_t vt[4 * S::MB];  // [t][mb][lo/hi]
     static_for<0, 2>([&](auto tc) {
@@ -317,12 +308,15 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) sv[rr] = acc[rr] * a.scale;
     }
-    // block max as a tree of three-input maxima (depth 3, not 8)
-    float t5[5];
+    // block max in two chains of three-input maxima (half the dependency depth
+    // of one chain, one register more)
+    float mb0 = __builtin_fmaxf(sv[0], sv[1]), mb1 = __builtin_fmaxf(sv[8], sv[9]);
 #pragma unroll
-    for (int q = 0; q < 5; ++q) t5[q] = __builtin_fmaxf(__builtin_fmaxf(sv[3 * q], sv[3 * q + 1]), sv[3 * q + 2]);
-    float mb = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(t5[0], t5[1]), t5[2]),
-                               __builtin_fmaxf(__builtin_fmaxf(t5[3], t5[4]), sv[15]));
+    for (int rr = 2; rr < 8; ++rr) {
+      mb0 = __builtin_fmaxf(mb0, sv[rr]);
+      mb1 = __builtin_fmaxf(mb1, sv[rr + 8]);
+    }
+    float mb = __builtin_fmaxf(mb0, mb1);
     mb = xhalf_max(mb);
     const bool need = mb > m_used + kTauNat;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -343,7 +337,8 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr], kLog2e, neg_ml));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr + 1], kLog2e, neg_ml));
       pk[rr / 2] = T::pack2(p0, p1);
-      if ((rr / 2) & 1) {
+      // fp16: two chains of v_dot2; bf16 sums in fp32 (its register budget is tighter)
+      if (std::is_same<T, F16>::value && ((rr / 2) & 1)) {
         l_part2 = T::rowsum_add(l_part2, p0, p1, pk[rr / 2]);
       } else {
         l_part = T::rowsum_add(l_part, p0, p1, pk[rr / 2]);
@@ -402,13 +397,13 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
     // blocks of the tile, software-pipelined: while block jb is in its softmax,
     // the QK^T MFMAs of block jb+1 run and the K operands and mask term of
     // block jb+2 load
-    const int nblk = min(TL::CH, L - kc0 + 31) / 32;
-    // dead-block bytes of this tile, wave-uniform
-    uint32_t dead_lo = 0, dead_hi = 0;
+    // blocks up to the tile's last key that is not -inf
+    int nblk = min(TL::CH, L - kc0 + 31) / 32;
     if constexpr (HAS_MASK) {
-      const u32x2 dw = *reinterpret_cast<const u32x2*>(&sdead[tb][0]);
-      dead_lo = __builtin_amdgcn_readfirstlane(dw[0]);
-      dead_hi = __builtin_amdgcn_readfirstlane(TL::CH / 32 > 4 ? dw[1] : 0u);
+      const u32x4 lv = *reinterpret_cast<const u32x4*>(&slive[tb][0]);
+      const int le = TL::CH > 128 ? max(max((int)lv[0], (int)lv[1]), max((int)lv[2], (int)lv[3]))
+                                  : max((int)lv[0], (int)lv[1]);
+      nblk = min(nblk, (__builtin_amdgcn_readfirstlane(le) + 31) / 32);
     }
     {
       constexpr int NB = (RES > 0 && RES < TL::CH / 32) ? RES : TL::CH / 32;
@@ -436,13 +431,12 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
           // the K operands of block jb + 2 are read only when it exists
           const bool pre_live = jb + 2 < nblk;
           constexpr int jpre = jb + 2 < NB ? jb + 2 : -1;
-          const bool live = (((jb < 4 ? dead_lo : dead_hi) >> (8 * (jb & 3))) & 0xffu) == 0u;
           if constexpr (RES > 0) {
             softmax_pv(sacc[jb & 1], tb, jbc, pres[jb < RES ? jb : 0], kreg[jb & 1], mc,
-                       std::integral_constant<int, jpre>{}, pre_live, live);
+                       std::integral_constant<int, jpre>{}, pre_live);
           } else {
             softmax_pv(sacc[jb & 1], tb, jbc, ptile[HAS_PAIR ? jb : 0], kreg[jb & 1], mc,
-                       std::integral_constant<int, jpre>{}, pre_live, live);
+                       std::integral_constant<int, jpre>{}, pre_live);
           }
         }
       });

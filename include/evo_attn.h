@@ -71,11 +71,12 @@ typedef enum {
  *   lse         [B,N,H,L]   float32        natural-log log-sum-exp of each row of S, or NULL
  * A query row whose scores are all -inf gets out = 0 and lse = -inf.  A key whose mask
  * bias is -inf (fp16's rounding of -1e9, or an explicit -inf) has P = 0 in every row: it
- * adds nothing to out, lse, dq or dpair, and gets dk = dv = dmask = 0.  Runs of such keys
- * (32 aligned keys in the forward and on the query side of the backward, a workgroup
- * wave's 16 keys on the key side) are skipped, so a padded batch masked with -inf costs
- * less than its full length (the block-sparse key masks of the block-sparse attention
- * page, at block granularity).  A finite mask, however large, is computed.  With lse NULL the
+ * adds nothing to out, lse, dq or dpair, and gets dk = dv = dmask = 0.  The 32-key blocks
+ * past the last key of a key tile (256 keys, 128 at D = 64) that is not -inf are not
+ * computed, and on the key side of the backward neither is a group of 16 keys that are all
+ * -inf, so a padded batch masked with -inf costs less than its full length (the
+ * block-sparse key masks of the block-sparse attention page, for padding).  A finite
+ * mask, however large, is computed.  With lse NULL the
  * call is a forward for inference (the guide's §3.2 notes the forward kernels pay off
  * at inference for every attention type): out is the same, bit for bit, and nothing is
  * kept for a backward. */
