@@ -1,13 +1,15 @@
 """Blocks of keys masked with -inf: parity with the oracle where the kernels skip work.
 
 A key whose mask bias is -inf has P = 0 in every row, so it adds nothing to O,
-lse, dQ or dpair, and its dK, dV and dmask are zero.  The kernels skip a
-32-key block (forward, query-side backward) or a wave's 16 keys (key-side
-backward) when every key in it is -inf.  These cases put such blocks where
-the skip paths run: padded batches (fp16, where -1e9 overflows to -inf, and
-bf16 with an explicit -inf), interior dead blocks, a whole slice with every key
-masked (O = 0, lse = -inf, zero gradients), rows of one and of several key
-tiles, D = 16, 32 and 64, with and without the pair bias.  Tolerances and the
+lse, dQ or dpair, and its dK, dV and dmask are zero.  The forward and the
+query-side backward stop each key tile at its last key that is not -inf (the
+32-key blocks past it are not computed), and a key-side backward wave whose 16
+keys are all -inf skips the slice.  These cases put masked keys where those
+paths run: padded batches (fp16, where -1e9 overflows to -inf, and bf16 with an
+explicit -inf), whole key tiles past a row's padding, interior blocks of -inf
+keys (computed, and exact either way), a whole slice with every key masked
+(O = 0, lse = -inf, zero gradients), rows of one and of several key tiles,
+D = 8, 16, 32 and 64, with and without the pair bias.  Tolerances and the
 comparison are those of the other parity tests.
 """
 import numpy as np
