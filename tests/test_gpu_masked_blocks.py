@@ -78,3 +78,39 @@ def test_parity_interior_dead_blocks(cfg, blocks, dead_slices):
         assert bool(np.isneginf(res["lse"][b, n].cpu().numpy()).all()), "lse of the fully masked slice"
         if res["dmask"] is not None:
             assert not bool(res["dmask"][b, n].any()), "dmask of the fully masked slice is not zero"
+
+
+TRUNC = [
+    (I.custom("trunc_l256_d32", 1, 3, 256, 2, 32, "fp16", 0.05, 1.0, 61), 150),
+    (I.custom("trunc_l600_d16", 1, 2, 600, 1, 16, "fp16", 0.05, 1.0, 62), 300),
+    (I.custom("trunc_l200_d64_bf16", 1, 2, 200, 2, 64, "bf16", 0.05, 1.0, 63, mask_value=NEG_INF), 77),
+]
+
+
+@pytest.mark.parametrize("cfg,n_keys", TRUNC, ids=[c[0].name for c in TRUNC])
+def test_padding_equals_truncation(cfg, n_keys):
+    """Keys past n_keys masked with -inf give, for the first n_keys queries, the same O, lse and dQ bits
+    as the same problem cut to length n_keys (the padding is skipped, not computed as zeros)."""
+    import torch
+
+    print(f"case truncation {cfg.name} shape={cfg.shape} dtype={cfg.dtype} n_keys={n_keys}", flush=True)
+    bits = I.make_inputs(cfg)
+    ninf = I.to_bits(np.array([NEG_INF], np.float32), cfg.dtype)[0]
+    bits["mask_bias"] = bits["mask_bias"].copy()
+    bits["mask_bias"][..., n_keys:] = ninf
+    n = n_keys
+    cut = {
+        "q": bits["q"][:, :, :n], "k": bits["k"][:, :, :n], "v": bits["v"][:, :, :n], "dout": bits["dout"][:, :, :n],
+        "mask_bias": bits["mask_bias"][..., :n], "pair_bias": bits["pair_bias"][..., :n, :n],
+    }
+    B, N, L, H, D = cfg.shape
+    cfg_cut = I.custom(cfg.name + "_cut", B, N, n, H, D, cfg.dtype, cfg.mask_p, cfg.pair_sigma, cfg.seed)
+    full = _run_gpu(cfg, bits)
+    short = _run_gpu(cfg_cut, cut)
+    assert torch.equal(full["out"][:, :, :n], short["out"]), "O differs from the truncated problem"
+    assert torch.equal(full["lse"][..., :n], short["lse"]), "lse differs from the truncated problem"
+    assert torch.equal(full["dq"][:, :, :n], short["dq"]), "dQ differs from the truncated problem"
+    # dpair sums over n in workgroup groups that depend on the row length: equal up to rounding
+    d_full = full["dpair32"][:, :, :, :n, :n].double().cpu().numpy()
+    d_short = short["dpair32"].double().cpu().numpy()
+    assert np.max(np.abs(d_full - d_short)) <= 1e-4, "dpair differs from the truncated problem"
