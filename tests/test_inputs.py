@@ -56,3 +56,22 @@ def test_config_shapes_and_fractions():
     assert 0.04 < frac < 0.06
     assert I.CONFIGS["msa_col"].pair_sigma is None
     assert I.make_inputs(I.custom("np", 1, 2, 4, 1, 8, pair_sigma=None))["pair_bias"] is None
+
+
+def test_padded_batches_mask_past_each_length():
+    """Keys at or past an entry's length are masked in every row of it; the keys before keep the random
+    mask of the same seed without padding (the padding draws nothing)."""
+    for cfg in (I.PADDED, I.PADDED_UNIFORM):
+        x = I.as_float64(I.make_inputs(cfg), cfg.dtype)["mask_bias"][:, :, 0, 0, :]
+        for b, n_keys in enumerate(cfg.key_lengths):
+            assert np.isneginf(x[b, :, n_keys:]).all()
+            assert (x[b, :, :n_keys] == 0).mean() > 0.9
+    cfg = I.custom("p", 2, 3, 40, 1, 8, "bf16", 0.1, None, 5, key_lengths=(40, 9), mask_value=float("-inf"))
+    plain = I.custom("p", 2, 3, 40, 1, 8, "bf16", 0.1, None, 5, mask_value=float("-inf"))
+    a = I.as_float64(I.make_inputs(cfg), "bf16")
+    p = I.as_float64(I.make_inputs(plain), "bf16")
+    assert np.isneginf(a["mask_bias"][1, :, 0, 0, 9:]).all()
+    assert np.array_equal(a["mask_bias"][0], p["mask_bias"][0])
+    assert np.array_equal(a["mask_bias"][1, :, :, :, :9], p["mask_bias"][1, :, :, :, :9])
+    for key in ("q", "k", "v", "dout"):
+        assert np.array_equal(a[key], p[key])
