@@ -186,28 +186,41 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       }
     }
   };
-  // issue the asynchronous copy of tile t into LDS buffer (t & 1)
+  // issue the asynchronous copy of tile t into LDS buffer (t & 1): a uniform
+  // base pointer (the tile's first key row of the slice) plus a 32-bit byte
+  // offset per 16-byte chunk (K-layout chunks, then V-layout chunks; rows past
+  // L clamp to L - 1), so the copies address by scalar base + vector offset
+  constexpr int NCH = TL::TCH / 256;  // chunks per thread
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t sl2 = (uint32_t)a.sL * 2u, hd2 = (uint32_t)(h * D) * 2u;
   auto issue_tile = [&](int t) {
+    const int c = t % nchunks;
     const int n = n_begin + t / nchunks;
-    const int kc0 = (t % nchunks) * TL::CH;
-    const int64_t slice = b * a.sB + n * a.sN + h * D;  // element offset of key 0's head h
+    const int lim = min(TL::CH - 1, L - 1 - c * TL::CH);
+    const int64_t row0 = b * a.sB + n * a.sN + (int64_t)(c * TL::CH) * a.sL;
+    const char* kbase = reinterpret_cast<const char*>(a.k + row0);
+    const char* vbase = reinterpret_cast<const char*>(a.v + row0);
     uint8_t* buf = smem + (t & 1) * TL::BUF_BYTES;
-    for (int base = wave * 64; base < TL::TCH; base += 256) {
-      const int q = base + lane;
-      const uint16_t* src;
-      if (q < TL::KCH) {
-        const int r = q / TL::KC, pos = q % TL::KC;
-        const int c = pos ^ kv_swz<TL::KC>(r);
-        const int j = min(kc0 + r, L - 1);
-        src = a.k + slice + j * a.sL + 8 * c;
+    // the offsets are recomputed per tile (a few integer ops per chunk) rather
+    // than kept in registers across the tile loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int base = wave_u * 64 + 256 * i;  // wave-uniform
+      const int q = base + ln;
+      int r, cc;
+      if (base < TL::KCH) {
+        r = q / TL::KC;
+        cc = (q % TL::KC) ^ kv_swz<TL::KC>(r);
       } else {
         const int q2 = q - TL::KCH;
-        const int r = q2 / TL::VC, pos = q2 % TL::VC;
-        int c = pos ^ kv_swz<TL::VC>(r);
-        if (c >= D / 8) c = 0;  // columns the transposed reads touch but never use
-        const int j = min(kc0 + r, L - 1);
-        src = a.v + slice + j * a.sL + 8 * c;
+        r = q2 / TL::VC;
+        cc = (q2 % TL::VC) ^ kv_swz<TL::VC>(r);
+        if (cc >= D / 8) cc = 0;  // columns the transposed reads touch but never use
       }
+      const uint32_t off = (uint32_t)min(r, lim) * sl2 + hd2 + 16u * (uint32_t)cc;
+      const char* src = (base < TL::KCH ? kbase : vbase) + off;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(buf + base * 16), 16, 0, 0);
     }
