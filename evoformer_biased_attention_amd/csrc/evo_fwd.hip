@@ -90,6 +90,7 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // known uniform to the compiler
   const int half = lane >> 5;
   const int L = a.L, H = a.H, N = a.N;
 
@@ -125,14 +126,18 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
         // c ^ (r & 15), so the per-lane reads below are spread over the banks),
         // then every lane picks its values.  Runs before the first K/V tile.
         constexpr int RC = RES * 4;  // 16-byte chunks per staged row
-        const uint16_t* pbase = a.pair + ((size_t)b * H + h) * L * L;
         const int row0 = it * kFwdRows;
-        for (int base = wave * 64; base < kFwdRows * RC; base += 256) {
+        // uniform base (the slab's first row) plus a 32-bit offset per chunk
+        const char* pbase = reinterpret_cast<const char*>(a.pair + (((size_t)b * H + h) * L + row0) * L);
+        const int rlim = L - 1 - row0;
+#pragma unroll
+        for (int k = 0; k < kFwdRows * RC / 256; ++k) {
+          const int base = wave_u * 64 + 256 * k;
           const int q = base + lane;
           const int r = q / RC, pos = q % RC;
           const int c = min(pos ^ (r & 15), L / 8 - 1);
-          const uint16_t* src = pbase + (size_t)min(row0 + r, L - 1) * L + 8 * c;
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+          const uint32_t off = ((uint32_t)min(r, rlim) * (uint32_t)L + 8u * (uint32_t)c) * 2u;
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(pbase + off),
                                            (__attribute__((address_space(3))) void*)(smem + base * 16), 16, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(0);
@@ -191,7 +196,6 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
   // offset per 16-byte chunk (K-layout chunks, then V-layout chunks; rows past
   // L clamp to L - 1), so the copies address by scalar base + vector offset
   constexpr int NCH = TL::TCH / 256;  // chunks per thread
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t sl2 = (uint32_t)a.sL * 2u, hd2 = (uint32_t)(h * D) * 2u;
   auto issue_tile = [&](int t) {
     const int c = t % nchunks;
