@@ -254,12 +254,22 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     vm_wait_all();
     take_rows(n_begin);
   }
-  // The next slice's copies and row loads are completed, and its rows taken
-  // into the operand registers, before this slice's dQ stores are issued: no
-  // wait (the barrier's or the compiler's) then waits for those stores.
+  // The next slice's copies and row loads are completed before this slice's
+  // dQ stores are issued.  With SPLIT (one key tile of a longer row per
+  // workgroup, fp32 dQ partials) the next slice's rows are also taken then and
+  // the barrier waits for LDS only, so nothing waits for the stores; rows of
+  // one key tile measured faster with the plain barrier and the rows taken
+  // after it (A/B on one device: bwd_q3 -4% at L = 256, +10% with SPLIT at
+  // L = 768).
   for (int t = 0; t < ntiles; ++t) {
     const int n = n_begin + t;
-    lds_barrier();
+    if constexpr (SPLIT) {
+      lds_barrier();
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (t > 0) take_rows(n);
+    }
     if (t + 1 < ntiles) {
       issue_tile<D, NT>(smem + ((t + 1) & 1) * TL::BUF_BYTES, slice_ptr(a.k, n + 1), slice_ptr(a.v, n + 1), coff, wave);
       load_rows(n + 1);
@@ -404,7 +414,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     vm_wait_all();  // the next slice's copies and row loads
     if (t + 1 < ntiles) {
       store_mask((t + 1) & 1);  // its buffer was last read during slice t-1
-      take_rows(n + 1);
+      if constexpr (SPLIT) take_rows(n + 1);
     }
     // ---- dQ = scale * dQ^T: lane holds d = 16 mb + 4 g + 0..3 of query i
     if (i_valid) {
