@@ -286,7 +286,7 @@ def main():
                 "speedup_vs_unpadded": round(ms_step / ms_s, 3), "fwd_speedup_vs_unpadded": round(ms_fwd / ms_f, 3),
                 "workload": f"{pcfg.name}: Q,K,V {list(pcfg.shape)} {pcfg.dtype}, key lengths "
                             f"{list(pcfg.key_lengths)} of {pcfg.L}, mask p={pcfg.mask_p}, seed {pcfg.seed}",
-                "note": "fwd+bwd step; 32-key blocks whose keys are all -inf are skipped"}
+                "note": "fwd+bwd step; the 32-key blocks past each key tile's last key that is not -inf are skipped"}
 
     pad_uniform = padded(I.PADDED_UNIFORM)
     pad_mixed = padded(I.PADDED)
