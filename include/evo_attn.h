@@ -75,8 +75,9 @@ typedef enum {
  * past the last key of a key tile (256 keys, 128 at D = 64) that is not -inf are not
  * computed, and on the key side of the backward neither is a group of 16 keys that are all
  * -inf, so a padded batch masked with -inf costs less than its full length (the
- * block-sparse key masks of the block-sparse attention page, for padding).  A finite
- * mask, however large, is computed.  With lse NULL the
+ * block-sparse principle of the page "DeepSpeed Sparse Attention 深度解析", section
+ * 核心思想: only the blocks a mask leaves are computed; applied here to padding).  A
+ * finite mask, however large, is computed.  With lse NULL the
  * call is a forward for inference (the guide's §3.2 notes the forward kernels pay off
  * at inference for every attention type): out is the same, bit for bit, and nothing is
  * kept for a backward. */
