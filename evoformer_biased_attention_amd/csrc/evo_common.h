@@ -159,11 +159,6 @@ __device__ __forceinline__ uint32_t xhalf_partner(uint32_t x) {
   const bool lo = (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) < 32);
   return __builtin_bit_cast(uint32_t, lo ? b : a);
 }
-__device__ __forceinline__ float xhalf_max(float x) {
-  float a = x, b = x;
-  xhalf_swap(a, b);
-  return __builtin_fmaxf(a, b);
-}
 __device__ __forceinline__ float xhalf_sum(float x) {
   float a = x, b = x;
   xhalf_swap(a, b);

@@ -326,15 +326,27 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       for (int rr = 0; rr < 16; ++rr) sv[rr] = acc[rr] * a.scale;
     }
     // block max in two chains of three-input maxima (half the dependency depth
-    // of one chain, one register more)
-    float mb0 = __builtin_fmaxf(sv[0], sv[1]), mb1 = __builtin_fmaxf(sv[8], sv[9]);
-#pragma unroll
-    for (int rr = 2; rr < 8; ++rr) {
-      mb0 = __builtin_fmaxf(mb0, sv[rr]);
-      mb1 = __builtin_fmaxf(mb1, sv[rr + 8]);
+    // of one chain).  Written as assembly: the scores come out of assembly
+    // (v_fma_mix_f32), so the compiler would first canonicalize them for its
+    // own maximum (four extra instructions per block); scores are never NaN
+    // for finite inputs.
+    auto max3 = [](float x, float y, float z) {
+      float r;
+      asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+      return r;
+    };
+    float mb0 = max3(sv[0], sv[1], sv[2]), mb1 = max3(sv[8], sv[9], sv[10]);
+    mb0 = max3(mb0, sv[3], sv[4]);
+    mb1 = max3(mb1, sv[11], sv[12]);
+    mb0 = max3(mb0, sv[5], sv[6]);
+    mb1 = max3(mb1, sv[13], sv[14]);
+    mb0 = max3(mb0, mb1, sv[7]);
+    float mb = max3(mb0, sv[15], sv[15]);
+    {  // with the partner half (lane ^ 32) holding the same query row
+      float pa = mb, pb = mb;
+      xhalf_swap(pa, pb);
+      mb = max3(pa, pb, pb);
     }
-    float mb = __builtin_fmaxf(mb0, mb1);
-    mb = xhalf_max(mb);
     const bool need = mb > m_used + kTauNat;
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float m_new = need ? mb : m_used;
