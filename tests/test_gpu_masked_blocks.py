@@ -114,3 +114,17 @@ def test_padding_equals_truncation(cfg, n_keys):
     d_full = full["dpair32"][:, :, :, :n, :n].double().cpu().numpy()
     d_short = short["dpair32"].double().cpu().numpy()
     assert np.max(np.abs(d_full - d_short)) <= 1e-4, "dpair differs from the truncated problem"
+
+
+@pytest.mark.parametrize("cfg", [I.PADDED_UNIFORM, I.PADDED], ids=["padded_uniform", "padded_mixed"])
+def test_parity_benchmark_padded_workloads(cfg):
+    """The two padded workloads the benchmark times, at full size: every output of 16 sampled
+    dim-1 slices, and 32 sampled dpair rows (summed over all slices)."""
+    print(f"case padded workload {cfg.name} shape={cfg.shape} dtype={cfg.dtype} lengths={cfg.key_lengths}",
+          flush=True)
+    bits = I.make_inputs(cfg)
+    res = _run_gpu(cfg, bits)
+    rng = np.random.default_rng(1107)
+    ns = sorted(rng.choice(cfg.N, 16, replace=False).tolist())
+    rows = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H)), int(rng.integers(cfg.L))) for _ in range(32)]
+    _compare(cfg, bits, res, ns=ns, dpair_rows=rows)
