@@ -15,6 +15,20 @@ LIB_PATH = os.path.join(HERE, "libevoattn.so")
 EVO_F16 = 0
 EVO_BF16 = 1
 
+# status codes (include/evo_attn.h)
+EVO_OK = 0
+EVO_ERR_NULL_POINTER = 1
+EVO_ERR_BAD_SHAPE = 2
+EVO_ERR_BAD_DTYPE = 3
+EVO_ERR_HEAD_DIM = 4
+EVO_ERR_ALIGNMENT = 5
+EVO_ERR_NOT_DEVICE_MEMORY = 6
+EVO_ERR_WORKSPACE = 7
+EVO_ERR_DEVICE = 8
+EVO_ERR_LAUNCH = 9
+EVO_ERR_ALIAS = 10
+EVO_ERR_BAD_STRIDES = 11
+
 EXPORTED = (
     "evo_attn_fwd",
     "evo_attn_bwd",

@@ -67,6 +67,20 @@ def _layout(ts) -> Optional[Tuple[int, int, int]]:
     return tuple(x if e > 1 else 8 for x, e in zip(st[:3], (B, N, L)))
 
 
+def _aligned(t: Optional[torch.Tensor], contiguous: bool = False) -> Optional[torch.Tensor]:
+    """``t`` itself when the library can take it, else a fresh copy: the C ABI needs
+    16-byte aligned pointers, which a valid view at an odd element offset (a
+    slice of a larger tensor) does not have.  ``contiguous`` also makes the
+    result dense row-major (the bias and lse layouts the library assumes)."""
+    if t is None:
+        return None
+    if contiguous:
+        t = t.contiguous()
+    if t.data_ptr() % 16 != 0:
+        t = t.clone(memory_format=torch.contiguous_format if contiguous else torch.preserve_format)
+    return t
+
+
 def _dense_strides(shape) -> Tuple[int, int, int]:
     B, N, L, H, D = shape
     return (N * L * H * D, L * H * D, H * D)
@@ -85,8 +99,9 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_bias: Optio
     if lay is None:
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         lay = _dense_strides(q.shape)
-    mask_bias = None if mask_bias is None else mask_bias.contiguous()
-    pair_bias = None if pair_bias is None else pair_bias.contiguous()
+    q, k, v = _aligned(q), _aligned(k), _aligned(v)
+    mask_bias = _aligned(mask_bias, contiguous=True)
+    pair_bias = _aligned(pair_bias, contiguous=True)
     B, N, L, H, D = q.shape
     out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, N, H, L), dtype=torch.float32, device=q.device) if need_lse else None
@@ -104,11 +119,12 @@ def attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask: bool = T
     if lay is None:
         q, k, v, out = (t.contiguous() for t in (q, k, v, out))
         lay = _dense_strides(q.shape)
-    if dout.stride() != q.stride():
+    q, k, v, out = _aligned(q), _aligned(k), _aligned(v), _aligned(out)
+    if dout.stride() != q.stride() or dout.data_ptr() % 16 != 0:
         dout = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device).copy_(dout)
-    lse = lse.contiguous()
-    mask_bias = None if mask_bias is None else mask_bias.contiguous()
-    pair_bias = None if pair_bias is None else pair_bias.contiguous()
+    lse = _aligned(lse, contiguous=True)
+    mask_bias = _aligned(mask_bias, contiguous=True)
+    pair_bias = _aligned(pair_bias, contiguous=True)
     B, N, L, H, D = q.shape
     dt = _DT[q.dtype]
     dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) for _ in range(3))

@@ -154,13 +154,6 @@ Range rng(const void* p, int64_t bytes) {
 
 
 
-int env_int(const char* name, int dflt) {
-  const char* s = std::getenv(name);
-  if (!s || !*s) return dflt;
-  int v = std::atoi(s);
-  return v > 0 ? v : dflt;
-}
-
 // slices per forward workgroup: about two workgroups per CU (512), and never
 // more than 4 slices each (measured on MI355X: larger groups lose more to the
 // tail of the grid than they gain from reusing the pair bias)
@@ -170,7 +163,7 @@ int plan_fwd_group(const Shape& s) {
   if (g < 1) g = 1;
   if (g > 4) g = 4;
   if (g > s.N) g = s.N;
-  return env_int("EVOATTN_FWD_G", (int)g);
+  return (int)g;
 }
 
 // keys per backward tile (KVTile<D>::CH)
@@ -190,8 +183,7 @@ int plan_bwdq_group(const Shape& s) {
   for (int64_t k = 1; k <= kmax; ++k) best_t = std::min(best_t, cost(k));
   int64_t k = 1;
   while (k < kmax && cost(k) * 100 > best_t * 103) ++k;
-  const int64_t g = (s.N + k - 1) / k;
-  return env_int("EVOATTN_BWD_GQ", (int)g);
+  return (int)((s.N + k - 1) / k);
 }
 
 // slices per bwd_kv3 workgroup: same rule over the key-side grid (one

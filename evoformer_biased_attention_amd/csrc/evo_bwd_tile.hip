@@ -161,6 +161,11 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
       pbias[blk] = v;
     }
   }
+  // bf16: the n-sum of dpair adds the fp32 dS (the bf16-rounded dS, 2^-9
+  // relative, summed over N slices reaches the gradient tolerance where a
+  // row's probability sits on few keys); fp16 rounds 8x finer and keeps the
+  // identity MFMA
+  constexpr bool kDpairF32 = std::is_same<T, BF16>::value;
   // identity A operand of the 16x16x16 dpair MFMA: lane (row col, group g) holds A[col][4g + e]
   short4_t ident;
 #pragma unroll
@@ -401,8 +406,17 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
                           T::pack2(ds[1][2], ds[1][3])};
         const short8_t dsb = __builtin_bit_cast(short8_t, dw);
         if constexpr (WANT_DPAIR) {
-          dpacc[2 * st] = T::mfma16k16(ident, __builtin_bit_cast(short4_t, u32x2{dw[0], dw[1]}), dpacc[2 * st]);
-          dpacc[2 * st + 1] = T::mfma16k16(ident, __builtin_bit_cast(short4_t, u32x2{dw[2], dw[3]}), dpacc[2 * st + 1]);
+          if constexpr (kDpairF32) {
+            // accumulator register r of the identity product is the lane's own
+            // operand element r, so the n-sum is an fp32 add in place
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) dpacc[2 * st + hb][r] += ds[hb][r];
+          } else {
+            dpacc[2 * st] = T::mfma16k16(ident, __builtin_bit_cast(short4_t, u32x2{dw[0], dw[1]}), dpacc[2 * st]);
+            dpacc[2 * st + 1] = T::mfma16k16(ident, __builtin_bit_cast(short4_t, u32x2{dw[2], dw[3]}), dpacc[2 * st + 1]);
+          }
         }
         lgkm_wait<0>();
 #pragma unroll

@@ -82,3 +82,32 @@ def test_layout_slice_limit():
     ok, bad = (1 << 40, 1 << 40, 16384), (1 << 40, 1 << 40, 16392)
     assert _lib.evo_attn_fwd_strided(None, None, None, None, None, None, None, shape, ok, 0, None) == 1
     assert _lib.evo_attn_fwd_strided(None, None, None, None, None, None, None, shape, bad, 0, None) == 11
+
+
+_NO_DEVICE_PROBE = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+from evoformer_biased_attention_amd import _lib
+shape = (1, 2, 32, 2, 32)
+p = [16 * (i + 1) for i in range(14)]  # non-NULL, aligned; never dereferenced
+fwd = _lib.evo_attn_fwd(p[0], p[1], p[2], None, None, p[3], p[4], shape, _lib.EVO_F16, None)
+nws = _lib.evo_attn_bwd_workspace_bytes(shape, _lib.EVO_F16, 0, 0)
+bwd = _lib.evo_attn_bwd(p[0], p[1], p[2], None, None, p[3], p[4], p[5], p[6], p[7], p[8], None, None,
+                        p[9], nws, shape, _lib.EVO_F16, None)
+print(fwd, bwd)
+"""
+
+
+def test_no_usable_device_is_reported_as_evo_err_device():
+    """With no HIP device visible to the process, valid arguments reach the
+    library's device check (guide §3.7: inputs must live on the GPU the kernel
+    was built for), which answers EVO_ERR_DEVICE and enqueues nothing."""
+    import subprocess
+    import sys
+
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1")
+    r = subprocess.run([sys.executable, "-c", _NO_DEVICE_PROBE, ROOT], env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    fwd, bwd = (int(x) for x in r.stdout.split()[-2:])
+    assert fwd == _lib.EVO_ERR_DEVICE and bwd == _lib.EVO_ERR_DEVICE, r.stdout

@@ -169,6 +169,37 @@ def test_autograd_wrapper_equals_direct_calls():
     assert torch.equal(out_m, o3)
 
 
+def test_offset_views_are_taken():
+    """Valid views at an odd element offset (slices of larger tensors) have
+    pointers that are not 16-byte aligned, which the C ABI refuses; the Python
+    layer hands the library aligned copies, and the results equal those of the
+    aligned tensors bit for bit."""
+    from evoformer_biased_attention_amd.attention import attn_bwd, attn_fwd, evoformer_attention
+
+    cfg = I.custom("offset_l36", 1, 3, 36, 2, 16, "fp16", 0.2, 1.0, 42)
+    print(f"case offset views {cfg.name}", flush=True)
+    _, x = _inputs(cfg)
+
+    def offset(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        view = buf[1:].view(t.shape)
+        view.copy_(t)
+        assert view.data_ptr() % 16 != 0
+        return view
+
+    y = {n: offset(t) for n, t in x.items()}
+    o1, l1 = attn_fwd(x["q"], x["k"], x["v"], x["mask_bias"], x["pair_bias"])
+    o2, l2 = attn_fwd(y["q"], y["k"], y["v"], y["mask_bias"], y["pair_bias"])
+    g1 = attn_bwd(x["q"], x["k"], x["v"], x["mask_bias"], x["pair_bias"], o1, l1, x["dout"])
+    g2 = attn_bwd(y["q"], y["k"], y["v"], y["mask_bias"], y["pair_bias"], offset(o1), offset(l1), y["dout"])
+    with torch.no_grad():
+        o3 = evoformer_attention(y["q"], y["k"], y["v"], [y["mask_bias"], y["pair_bias"]])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3)
+    for key in ("dq", "dk", "dv", "dmask", "dpair"):
+        assert torch.equal(g1[key], g2[key]), key
+
+
 @pytest.mark.parametrize("cfg", [CASES[0], CASES[2], CASES[4], CASES[5]], ids=[c.name for c in (CASES[0], CASES[2], CASES[4], CASES[5])])
 def test_inference_forward_same_output(cfg):
     from evoformer_biased_attention_amd.attention import attn_fwd, evoformer_attention

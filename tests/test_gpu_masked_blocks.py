@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 from evoformer_biased_attention_amd import inputs as I
-from tests.test_gpu_parity import _compare, _run_gpu
+from tests.helpers import compare_with_oracle as _compare, run_gpu as _run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -118,13 +118,10 @@ def test_padding_equals_truncation(cfg, n_keys):
 
 @pytest.mark.parametrize("cfg", [I.PADDED_UNIFORM, I.PADDED], ids=["padded_uniform", "padded_mixed"])
 def test_parity_benchmark_padded_workloads(cfg):
-    """The two padded workloads the benchmark times, at full size: every output of 16 sampled
-    dim-1 slices, and 32 sampled dpair rows (summed over all slices)."""
+    """The two padded workloads the benchmark times, at full size: every element of every
+    output (dpair summed over all slices)."""
     print(f"case padded workload {cfg.name} shape={cfg.shape} dtype={cfg.dtype} lengths={cfg.key_lengths}",
           flush=True)
     bits = I.make_inputs(cfg)
     res = _run_gpu(cfg, bits)
-    rng = np.random.default_rng(1107)
-    ns = sorted(rng.choice(cfg.N, 16, replace=False).tolist())
-    rows = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H)), int(rng.integers(cfg.L))) for _ in range(32)]
-    _compare(cfg, bits, res, ns=ns, dpair_rows=rows)
+    _compare(cfg, bits, res)

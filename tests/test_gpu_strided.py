@@ -3,10 +3,9 @@
 Guide §3.6 names triangle attention around the ending node beside the
 starting-node form: the same operation on the pair representation transposed
 over its two residue axes.  With strides the library takes that transposed
-view as it is.  The arithmetic does not depend on where the rows sit, so every
-output must equal, bit for bit, the result of the dense layout on the same
-logical values (the dense path is checked against the oracle by the parity
-tests):
+view as it is.  Every output of a strided call is compared with the fp64 oracle evaluated on
+the logical tensors, and, since the arithmetic does not depend on where the
+rows sit, also with the dense layout's result bit for bit:
 
 * views transposed over N and L (the ending-node case) and permuted so that
   B is innermost, through the Python layer, forward and backward;
@@ -19,8 +18,8 @@ import torch
 
 from evoformer_biased_attention_amd import _lib
 from evoformer_biased_attention_amd import inputs as I
-from evoformer_biased_attention_amd.attention import attn_bwd, attn_fwd
-from tests.helpers import to_device
+from evoformer_biased_attention_amd.attention import attn_bwd, attn_fwd, workspace_f32_views
+from tests.helpers import compare_with_oracle, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -48,12 +47,33 @@ def _relayout(t, perm):
     return store.permute(*inv)
 
 
-def _run(x, q, k, v, dout):
+def _run(x, q, k, v, dout, with_ws=False):
     out, lse = attn_fwd(q, k, v, x["mask_bias"], x["pair_bias"])
     g = attn_bwd(q, k, v, x["mask_bias"], x["pair_bias"], out, lse, dout)
     torch.cuda.synchronize()
-    return {"out": out, "lse": lse, "dq": g["dq"], "dk": g["dk"], "dv": g["dv"], "dmask": g["dmask"],
-            "dpair": g["dpair"]}
+    res = {"out": out, "lse": lse, "dq": g["dq"], "dk": g["dk"], "dv": g["dv"], "dmask": g["dmask"],
+           "dpair": g["dpair"]}
+    if with_ws:
+        delta, dm32, dp32 = workspace_f32_views(g["workspace"], q.shape, q.dtype, x["mask_bias"] is not None,
+                                                x["pair_bias"] is not None)
+        res.update({"delta": delta.clone(), "dmask32": None if dm32 is None else dm32.clone(),
+                    "dpair32": None if dp32 is None else dp32.clone()})
+    return res
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
+def test_ending_node_views_against_oracle(cfg):
+    """Triangle attention around the ending node: Q, K, V, dO handed over as
+    views transposed over N and L (no copy) and every output, in the view's
+    layout, compared with the oracle on the logical values."""
+    print(f"case ending-node view vs oracle {cfg.name} shape={cfg.shape} dtype={cfg.dtype}", flush=True)
+    bits = I.make_inputs(cfg)
+    x = {n: to_device(bits[n], cfg.dtype) for n in ("q", "k", "v", "mask_bias", "pair_bias", "dout")}
+    q, k, v, do = (_relayout(x[n], [0, 2, 1]) for n in ("q", "k", "v", "dout"))
+    res = _run(x, q, k, v, do, with_ws=True)
+    for n in ("out", "dq", "dk", "dv"):
+        assert res[n].stride() == q.stride(), n
+    compare_with_oracle(cfg, bits, res)
 
 
 @pytest.mark.parametrize("perm", [(0, 2, 1), (2, 1, 0)], ids=["transposed_NL", "B_innermost"])
@@ -117,6 +137,11 @@ def test_padded_rows_through_the_c_abi(cfg):
         buf, view = outs[n]
         assert torch.equal(view, ref[n]), f"{n} differs from the dense layout"
         assert bool((buf[..., H * D:] == 7.0).all()), f"padding of {n} was written"
+    # the same outputs against the oracle on the logical values
+    delta, dm32, dp32 = workspace_f32_views(ws, cfg.shape, tdt, m is not None, p is not None)
+    res = {"out": outs["out"][1], "lse": lse, "dq": outs["dq"][1], "dk": outs["dk"][1], "dv": outs["dv"][1],
+           "dmask": dm, "dpair": dp, "delta": delta, "dmask32": dm32, "dpair32": dp32}
+    compare_with_oracle(cfg, I.make_inputs(cfg), res)
     assert torch.equal(lse, ref["lse"])
     if m is not None:
         assert torch.equal(dm, ref["dmask"])
