@@ -28,12 +28,15 @@ EVO_ERR_DEVICE = 8
 EVO_ERR_LAUNCH = 9
 EVO_ERR_ALIAS = 10
 EVO_ERR_BAD_STRIDES = 11
+EVO_ERR_SCRATCH_LIMIT = 12
+EVO_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = (
     "evo_attn_fwd",
     "evo_attn_bwd",
     "evo_attn_fwd_strided",
     "evo_attn_bwd_strided",
+    "evo_attn_bwd_noalloc",
     "evo_attn_bwd_workspace_bytes",
     "evo_attn_bwd_workspace_offsets",
     "evo_status_string",
@@ -70,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.evo_attn_fwd_strided.restype = I
     lib.evo_attn_bwd_strided.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, S, S, I, P]
     lib.evo_attn_bwd_strided.restype = I
+    lib.evo_attn_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, S, S, I, P]
+    lib.evo_attn_bwd_noalloc.restype = I
     lib.evo_attn_bwd_workspace_bytes.argtypes = [S, I, I, I]
     lib.evo_attn_bwd_workspace_bytes.restype = Z
     lib.evo_attn_bwd_workspace_offsets.argtypes = [S, I, I, I, ctypes.POINTER(Z), ctypes.POINTER(Z), ctypes.POINTER(Z)]
@@ -119,6 +124,12 @@ def evo_attn_bwd_strided(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, 
     return load().evo_attn_bwd_strided(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias,
                                        dpair_bias, workspace, workspace_bytes, shape_arg(shape),
                                        strides_arg(strides), dtype, stream)
+
+
+def evo_attn_bwd_noalloc(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias,
+                         shape, strides, dtype, stream) -> int:
+    return load().evo_attn_bwd_noalloc(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias,
+                                       dpair_bias, shape_arg(shape), strides_arg(strides), dtype, stream)
 
 
 def evo_attn_bwd_workspace_bytes(shape, dtype, has_mask, has_pair) -> int:

@@ -42,6 +42,35 @@ bool device_is_gfx950(int dev) {
   return g_dev_ok[dev] == 1;
 }
 
+// ------------------------------------------------ static backward scratch
+//
+// The backward's workspace for evo_attn_bwd_noalloc (callers that cannot
+// allocate device memory).  Every GPU the library runs on holds its own copy
+// until the process ends; calls on one GPU share it, so calls that overlap on
+// one GPU race.  Every byte a backward reads from it is written earlier in the
+// same call, so nothing needs clearing between calls.
+constexpr size_t kScratchBytes = (size_t)EVO_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// with that device current (the array's name is only a host-side stand-in).
+void* g_scratch_ptr[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+void* scratch_device_ptr(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      p = nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  });
+  return g_scratch_ptr[dev];
+}
+
 struct Shape {
   int64_t B, N, L, H, D;
 };
@@ -310,6 +339,9 @@ const char* evo_status_string(int status) {
     case EVO_ERR_LAUNCH: return "kernel launch failed";
     case EVO_ERR_ALIAS: return "an output overlaps an input or another output";
     case EVO_ERR_BAD_STRIDES: return "strides: not multiples of 8 elements, overlapping rows, or a slice past 2 GiB";
+    case EVO_ERR_SCRATCH_LIMIT:
+      return "evo_attn_bwd_noalloc: this backward needs more scratch than the library's static limit "
+             "(EVO_NOALLOC_SCRATCH_BYTES); call evo_attn_bwd with a workspace instead";
   }
   return "unknown status";
 }
@@ -389,11 +421,17 @@ evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const voi
                               workspace, workspace_bytes, shape, nullptr, dtype, stream);
 }
 
-evo_status_t evo_attn_bwd_strided(const void* q, const void* k, const void* v, const void* mask_bias,
-                                  const void* pair_bias, const void* out, const float* lse, const void* dout,
-                                  void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias, void* workspace,
-                                  size_t workspace_bytes, const int64_t shape[5], const int64_t strides[3],
-                                  int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward behind evo_attn_bwd_strided and evo_attn_bwd_noalloc.  With
+// use_scratch the workspace is this GPU's copy of the static `scratch` array
+// (workspace and workspace_bytes are ignored).
+evo_status_t bwd_impl(const void* q, const void* k, const void* v, const void* mask_bias, const void* pair_bias,
+                      const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      void* dmask_bias, void* dpair_bias, void* workspace, size_t workspace_bytes,
+                      const int64_t shape[5], const int64_t strides[3], int dtype, void* stream, bool use_scratch) {
   Shape s;
   evo_status_t st = parse_shape(shape, dtype, &s);
   if (st != EVO_OK) return st;
@@ -403,13 +441,24 @@ evo_status_t evo_attn_bwd_strided(const void* q, const void* k, const void* v, c
   if ((dmask_bias && !mask_bias) || (dpair_bias && !pair_bias)) return EVO_ERR_NULL_POINTER;
   const bool has_mask = mask_bias != nullptr, has_pair = pair_bias != nullptr;
   WsLayout w = ws_layout(s, has_mask, has_pair);
-  if (!workspace || workspace_bytes < w.total) return EVO_ERR_WORKSPACE;
+  if (use_scratch) {
+    if (w.total > kScratchBytes) return EVO_ERR_SCRATCH_LIMIT;
+  } else if (!workspace || workspace_bytes < w.total) {
+    return EVO_ERR_WORKSPACE;
+  }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return EVO_ERR_DEVICE;
   if (!device_is_gfx950(dev)) return EVO_ERR_DEVICE;
-  const void* ptrs[] = {q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias, workspace};
+  const void* ptrs[] = {q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias};
   for (const void* p : ptrs)
     if (p && (st = check_device_ptr(p, dev)) != EVO_OK) return st;
+  if (use_scratch) {
+    workspace = scratch_device_ptr(dev);
+    if (workspace == nullptr) return EVO_ERR_DEVICE;
+    workspace_bytes = kScratchBytes;
+  } else if ((st = check_device_ptr(workspace, dev)) != EVO_OK) {
+    return st;
+  }
   const int64_t tb = footprint_bytes(s, lay);
   const Range ins[] = {rng(q, tb),
                        rng(k, tb),
@@ -463,6 +512,27 @@ evo_status_t evo_attn_bwd_strided(const void* q, const void* k, const void* v, c
   a.scale = (float)(1.0 / std::sqrt((double)s.D));
   hipError_t e = evo::launch_bwd(a, (int)s.D, dtype == EVO_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? EVO_OK : EVO_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+evo_status_t evo_attn_bwd_strided(const void* q, const void* k, const void* v, const void* mask_bias,
+                                  const void* pair_bias, const void* out, const float* lse, const void* dout,
+                                  void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias, void* workspace,
+                                  size_t workspace_bytes, const int64_t shape[5], const int64_t strides[3],
+                                  int dtype, void* stream) {
+  return bwd_impl(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias, workspace,
+                  workspace_bytes, shape, strides, dtype, stream, false);
+}
+
+evo_status_t evo_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* mask_bias,
+                                  const void* pair_bias, const void* out, const float* lse, const void* dout,
+                                  void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias,
+                                  const int64_t shape[5], const int64_t strides[3], int dtype, void* stream) {
+  return bwd_impl(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias, nullptr, 0,
+                  shape, strides, dtype, stream, true);
 }
 
 int evo_attn_profile_enable(int on) {

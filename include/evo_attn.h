@@ -25,7 +25,10 @@
  *     take other layouts for the [B,N,L,H,D] tensors).  16-bit tensors hold IEEE
  *     half (EVO_F16) or bfloat16 (EVO_BF16) values; lse is float32.
  *   - All buffers are owned by the caller.  The library allocates no device
- *     memory and keeps no state between calls; calls are re-entrant.
+ *     memory and keeps no state between calls; calls are re-entrant.  The one
+ *     exception is evo_attn_bwd_noalloc, whose workspace is a static device
+ *     array of EVO_NOALLOC_SCRATCH_BYTES that every GPU holds while the library
+ *     is loaded.
  *   - Outputs are overwritten, never accumulated.  No output may alias an
  *     input or another output.
  *   - A bias pointer may be NULL: that bias is absent (treated as zero).
@@ -60,7 +63,8 @@ typedef enum {
   EVO_ERR_DEVICE = 8,            /* the current device is not gfx950 */
   EVO_ERR_LAUNCH = 9,            /* a kernel launch failed */
   EVO_ERR_ALIAS = 10,            /* an output overlaps an input or another output */
-  EVO_ERR_BAD_STRIDES = 11       /* strides not multiples of 8, rows that overlap, or a slice past 2 GiB */
+  EVO_ERR_BAD_STRIDES = 11,      /* strides not multiples of 8, rows that overlap, or a slice past 2 GiB */
+  EVO_ERR_SCRATCH_LIMIT = 12     /* evo_attn_bwd_noalloc: the problem needs more than EVO_NOALLOC_SCRATCH_BYTES */
 } evo_status_t;
 
 /* Forward (guide §3.5 and §3.7: fused attention that keeps O and the fp32 lse).
@@ -141,6 +145,24 @@ evo_status_t evo_attn_bwd_strided(const void* q, const void* k, const void* v, c
                                   void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias,
                                   void* workspace, size_t workspace_bytes, const int64_t shape[5],
                                   const int64_t strides[3], int dtype, void* stream);
+
+/* The backward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments and results are those of evo_attn_bwd_strided (strides NULL: the
+ * dense layout) without the workspace: the call allocates nothing and uses
+ * instead a static device array of EVO_NOALLOC_SCRATCH_BYTES bytes (64 MiB)
+ * that every GPU the library runs on holds until the process ends.  A problem
+ * whose evo_attn_bwd_workspace_bytes() exceeds that limit returns
+ * EVO_ERR_SCRATCH_LIMIT before anything is enqueued.  All calls on one GPU
+ * share its array, which keeps the last call's contents: calls that overlap
+ * on one GPU (on different streams, or from several threads) race and must be
+ * serialised by the caller.  The fp32 accumulators that
+ * evo_attn_bwd_workspace_offsets describes are not reachable through this call. */
+#define EVO_NOALLOC_SCRATCH_BYTES (64u << 20)
+evo_status_t evo_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* mask_bias,
+                                  const void* pair_bias, const void* out, const float* lse, const void* dout,
+                                  void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias,
+                                  const int64_t shape[5], const int64_t strides[3], int dtype, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* evo_status_string(int status);

@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(0, 12):
+    for s in range(0, 13):
         assert _lib.evo_status_string(s)
     assert _lib.evo_status_string(99) == "unknown status"
 
@@ -111,3 +111,16 @@ def test_no_usable_device_is_reported_as_evo_err_device():
     assert r.returncode == 0, r.stderr
     fwd, bwd = (int(x) for x in r.stdout.split()[-2:])
     assert fwd == _lib.EVO_ERR_DEVICE and bwd == _lib.EVO_ERR_DEVICE, r.stdout
+
+
+def test_noalloc_backward_refuses_problems_past_its_static_scratch():
+    """evo_attn_bwd_noalloc works inside a static device array of
+    EVO_NOALLOC_SCRATCH_BYTES; a problem whose workspace is larger is refused
+    with EVO_ERR_SCRATCH_LIMIT before any device call."""
+    big = (1, 768, 768, 4, 32)
+    assert _lib.evo_attn_bwd_workspace_bytes(big, _lib.EVO_BF16, 1, 1) > _lib.EVO_NOALLOC_SCRATCH_BYTES
+    p = [16 * (i + 1) for i in range(13)]
+    assert _lib.evo_attn_bwd_noalloc(*p, big, None, _lib.EVO_BF16, None) == _lib.EVO_ERR_SCRATCH_LIMIT
+    # argument errors come first, as in evo_attn_bwd
+    assert _lib.evo_attn_bwd_noalloc(*([None] * 13), (1, 2, 32, 2, 7), None, 0, None) == _lib.EVO_ERR_HEAD_DIM
+    assert "EVO_NOALLOC_SCRATCH_BYTES" in _lib.evo_status_string(_lib.EVO_ERR_SCRATCH_LIMIT)
