@@ -22,15 +22,43 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0
+# fp32 vector ALU issue rate: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz, one lane-op per lane and
+# clock (packed fp32 is not used), in units of 1e12 lane-ops/s
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "fwd+bwd TFLOP/s & % MFMA peak, Evoformer attn (1,256,256,4,32) fp16"
 
-# MFMA flops each kernel must do per score (D = head dim): the GEMMs it
-# performs on the score tile to produce its outputs.
+# The method's own MFMA flops per score (D = head dim), each GEMM credited once:
+# the forward's S = QK^T and O += PV; the backward's S and dP recomputed once
+# (credited to the query side), dQ there, dV and dK on the key side.  The key
+# side's own recompute of S and dP is not credited.  Sum over the backward:
+# 10 D per score = 2.5 x the forward.
 KERNEL_FLOPS_PER_SCORE = {
-    "fwd": lambda D: 4 * D,      # S = QK^T, O += PV
-    "bwd_kv": lambda D: 8 * D,   # S, dP = dO V^T, dV += P^T dO, dK += dS^T Q
-    "bwd_q": lambda D: 6 * D,    # S, dP, dQ += dS K
+    "fwd": lambda D: 4 * D,
+    "bwd_q": lambda D: 6 * D,
+    "bwd_kv": lambda D: 4 * D,
 }
+# The vector-ALU work each kernel must do per score, in wave64 lane-op slots
+# (v_exp_f32 counted as 2, its issue cost): bias add with the scale (1), the
+# exponent argument (1), the exponent (2); forward: row max (0.5, one 3-input
+# max per two scores), 16-bit packing of P (0.5), row sum (0.5, one dot2 per
+# two scores); query side: dS = P (dP - delta) (1), packing of dS (0.5); key
+# side: dS (1), packing of P and dS (1).
+KERNEL_ALU_OPS_PER_SCORE = {"fwd": 5.5, "bwd_q": 5.5, "bwd_kv": 6.0}
+
+
+def algorithmic_bytes(cfg):
+    """HBM bytes the method must move (forward, backward): the forward reads Q, K, V
+    and the biases and writes O and lse; the backward reads Q, K, V, O, dO, the
+    biases and lse, writes and reads delta once, and writes dQ, dK, dV and the
+    bias gradients.  The [B,N,H,L,L] tensors the method avoids are not counted."""
+    B, N, L, H, D = cfg.shape
+    t = B * N * L * H * D * 2
+    mask = B * N * L * 2 if cfg.mask_p is not None else 0
+    pair = B * H * L * L * 2 if cfg.pair_sigma is not None else 0
+    rows = B * N * H * L * 4
+    fwd = 3 * t + mask + pair + t + rows
+    bwd = 5 * t + mask + pair + rows + 2 * rows + 3 * t + mask + pair
+    return fwd, bwd
 
 
 def parse():
@@ -41,6 +69,8 @@ def parse():
     p.add_argument("--workload", default="msa_row")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-configs", action="store_true", help="skip the per-workload fwd/bwd lines")
+    p.add_argument("--calls", type=int, default=30, help="per-call timings for median / min (warm and cold)")
     p.add_argument("--pmc-steps", type=int, default=0,
                    help="run a 256 MiB copy (counter calibration) and this many eager steps, print nothing else; "
                         "for use under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
@@ -145,18 +175,25 @@ def cpu_baseline(cfg, bits, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    cores = len(os.sched_getaffinity(0))
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                             for i in libs)
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        pass
     return {
         "value": per_slice * done / el / 1e12,
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": f"{done} (b,n)-slice evaluations (cycling over the {cfg.B * cfg.N} slices of {cfg.name}), fwd+bwd in float64, {el:.1f} s",
+        "blas": blas,
+        "sample": f"{done} (b,n)-slice evaluations (cycling over the {cfg.B * cfg.N} slices of {cfg.name}), "
+                  f"fwd+bwd in float64 with NumPy, {el:.1f} s; cores = len(os.sched_getaffinity(0))",
     }
 
 
@@ -270,6 +307,35 @@ def main():
     del qt, kt, vt, dot, out_t, lse_t
     ms_bwd = timed(lambda: attn_bwd(q, k, v, m, p, out, lse, do, workspace=ws))
 
+    # ---- per call, warm and cold: each call between its own two events, the
+    # device kept busy before the first event (a spin, or the eviction write) so
+    # that the launch itself is not timed; cold writes 1 GiB between calls (four
+    # times the 256 MB last-level cache), warm runs the calls on resident data
+    flush = torch.empty(1 << 29, dtype=torch.float16, device=dev)
+
+    def per_call(fn, cold, n=None):
+        n = n or args.calls
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for _ in range(2):
+            fn()
+        for i, (a, b) in enumerate(evs):
+            if cold:
+                flush.fill_(float(i % 5))
+            else:
+                torch.cuda._sleep(100000)
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in evs)
+        return {"median_ms": round(t[len(t) // 2], 5), "min_ms": round(t[0], 5)}
+
+    calls = {}
+    for name, fn in (("fwd", lambda: attn_fwd(q, k, v, m, p)),
+                     ("bwd", lambda: attn_bwd(q, k, v, m, p, out, lse, do, workspace=ws)),
+                     ("step", step)):
+        calls[name] = {"warm": per_call(fn, False), "cold": per_call(fn, True)}
+
     # ---- padded batches of the same shape and score count (fp16 -inf masks past
     # each entry's length): the kernels skip the 32-key blocks whose keys are all masked
     def padded(pcfg):
@@ -289,42 +355,121 @@ def main():
     pad_uniform = padded(I.PADDED_UNIFORM)
     pad_mixed = padded(I.PADDED)
 
-    # ---- per-kernel launch times: HIP events the library records on this
-    # stream around each of its kernels, over K more eager steps
-    _lib.evo_attn_profile_read()
-    _lib.evo_attn_profile_enable(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    _lib.evo_attn_profile_enable(False)
-    kern = _lib.evo_attn_profile_read()
+    def kernel_times(fn, n):
+        """Average launch time per kernel kind from the HIP events the library
+        records on this stream around each of its kernels."""
+        _lib.evo_attn_profile_read()
+        _lib.evo_attn_profile_enable(True)
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        _lib.evo_attn_profile_enable(False)
+        return {name: (1e3 * ms / cnt, cnt) for name, (ms, cnt) in _lib.evo_attn_profile_read().items() if cnt}
+
+    # ---- every workload of the evaluation, forward and backward per call (warm)
+    per_config = {}
+    if not args.no_configs:
+        for name in I.CONFIG_ORDER:
+            c = I.CONFIGS[name]
+            cb = I.make_inputs(c)
+            cdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[c.dtype]
+
+            def ct(x):
+                return None if x is None else torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(cdt)
+
+            cq, ck, cv, cm, cp, cdo = (ct(cb[n]) for n in ("q", "k", "v", "mask_bias", "pair_bias", "dout"))
+            del cb
+            co, cl = attn_fwd(cq, ck, cv, cm, cp)
+            cws = attn_bwd(cq, ck, cv, cm, cp, co, cl, cdo)["workspace"]
+            ncall = 10 if c.scores > 1e9 else args.calls
+            f_ = per_call(lambda: attn_fwd(cq, ck, cv, cm, cp), False, ncall)
+            b_ = per_call(lambda: attn_bwd(cq, ck, cv, cm, cp, co, cl, cdo, workspace=cws), False, ncall)
+            kt_ = kernel_times(lambda: (attn_fwd(cq, ck, cv, cm, cp),
+                                        attn_bwd(cq, ck, cv, cm, cp, co, cl, cdo, workspace=cws)), 5)
+            F_ = c.fwd_flops
+            tf_f = F_ / (f_["median_ms"] * 1e-3) / 1e12
+            tf_b = 2.5 * F_ / (b_["median_ms"] * 1e-3) / 1e12
+            per_config[name] = {
+                "shape": list(c.shape), "dtype": c.dtype, "pair_bias": c.pair_sigma is not None,
+                "fwd": {**f_, "tflops": round(tf_f, 2), "pct_peak": round(100 * tf_f / PEAK_MFMA_TFLOPS, 2)},
+                "bwd": {**b_, "tflops": round(tf_b, 2), "pct_peak": round(100 * tf_b / PEAK_MFMA_TFLOPS, 2)},
+                "kernel_us": {kk: round(vv[0], 2) for kk, vv in kt_.items()},
+                "workspace_bytes": int(cws.numel()),
+            }
+            del cq, ck, cv, cm, cp, cdo, co, cl, cws
+            torch.cuda.empty_cache()
+
+    # ---- per-kernel launch times of the metric workload over K more eager steps
+    kern = kernel_times(step, args.steps)
 
     F = cfg.fwd_flops
     tf_step = 3.5 * F / (ms_step * 1e-3) / 1e12
     tf_fwd = F / (ms_fwd * 1e-3) / 1e12
     tf_bwd = 2.5 * F / (ms_bwd * 1e-3) / 1e12
 
-    # ---- roofline of the dominant kernel
+    # ---- roofline of the dominant kernel, and of the forward and backward as wholes
     sha = kernel_sources_sha()
-    kernels = {name: {"avg_us": 1e3 * ms / n, "launches": n, "share": 0.0} for name, (ms, n) in kern.items() if n}
+    kernels = {name: {"avg_us": us, "launches": n, "share": 0.0} for name, (us, n) in kern.items()}
     tot = sum(v_["avg_us"] * v_["launches"] for v_ in kernels.values()) or 1.0
-    # kernel time share of the step, per kernel
     for v_ in kernels.values():
         v_["share"] = v_["avg_us"] * v_["launches"] / tot
-    dom = max((n for n in kernels if n in KERNEL_FLOPS_PER_SCORE), key=lambda n: kernels[n]["share"])
+    dom = max((n for n in kernels if n in KERNEL_ALU_OPS_PER_SCORE), key=lambda n: kernels[n]["share"])
+    dom_us = kernels[dom]["avg_us"]
+    ops_launch = KERNEL_ALU_OPS_PER_SCORE[dom] * cfg.scores
     flops_launch = KERNEL_FLOPS_PER_SCORE[dom](cfg.D) * cfg.scores
-    achieved = flops_launch / (kernels[dom]["avg_us"] * 1e-6) / 1e12
+    alu = ops_launch / (dom_us * 1e-6) / 1e12
+    dom_traffic = load_traffic(dom, cfg.name, sha)
     roofline = {
         "kernel": dom,
-        "bound": "mfma",
-        "achieved": round(achieved, 2),
-        "peak": PEAK_MFMA_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
-        "traffic": load_traffic(dom, cfg.name, sha),
-        "flops_per_launch": flops_launch,
-        "avg_launch_us": round(kernels[dom]["avg_us"], 2),
+        "bound": "alu",
+        "achieved": round(alu, 3),
+        "peak": round(PEAK_VALU_TOPS, 3),
+        "unit": "T lane-ops/s (fp32 vector ALU, v_exp_f32 counted as 2)",
+        "frac": round(alu / PEAK_VALU_TOPS, 4),
+        "traffic": dom_traffic,
+        "alu_ops_per_launch": ops_launch,
+        "avg_launch_us": round(dom_us, 2),
+        "mfma": {"achieved_tflops": round(flops_launch / (dom_us * 1e-6) / 1e12, 2), "peak_tflops": PEAK_MFMA_TFLOPS,
+                 "frac": round(flops_launch / (dom_us * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                 "flops_per_launch": flops_launch},
     }
+    fwd_b, bwd_b = algorithmic_bytes(cfg)
+    bwd_kinds = [n for n in kernels if n.startswith("bwd")]
+    t_fwd_k = kernels["fwd"]["avg_us"] * 1e-6
+    t_bwd_k = sum(kernels[n]["avg_us"] for n in bwd_kinds) * 1e-6
+
+    def hbm(alg, t, kinds):
+        cnt = [load_traffic(n, cfg.name, sha) for n in kinds]
+        counted = None if any(x is None for x in cnt) else int(sum(cnt))
+        return {"algorithmic_bytes": alg, "achieved_gbs": round(alg / t / 1e9, 1),
+                "frac": round(alg / t / 1e9 / PEAK_HBM_GBS, 4), "counter_bytes": counted,
+                "traffic_ratio": None if counted is None else round(counted / alg, 3)}
+
+    wholes = {
+        "fwd": {"kernel_us": round(t_fwd_k * 1e6, 2),
+                "mfma_frac": round(F / t_fwd_k / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                "alu_frac": round(KERNEL_ALU_OPS_PER_SCORE["fwd"] * cfg.scores / t_fwd_k / 1e12 / PEAK_VALU_TOPS, 4),
+                "hbm": hbm(fwd_b, t_fwd_k, ["fwd"])},
+        "bwd": {"kernel_us": round(t_bwd_k * 1e6, 2),
+                "mfma_frac": round(2.5 * F / t_bwd_k / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                "alu_frac": round((KERNEL_ALU_OPS_PER_SCORE["bwd_q"] + KERNEL_ALU_OPS_PER_SCORE["bwd_kv"])
+                                  * cfg.scores / t_bwd_k / 1e12 / PEAK_VALU_TOPS, 4),
+                "hbm": hbm(bwd_b, t_bwd_k, bwd_kinds)},
+    }
+
+    # ---- a library GEMM rate on the same device, for reference next to the spec peak
+    ga = torch.randn(8192, 8192, dtype=torch.float16, device=dev)
+    gb = torch.randn(8192, 8192, dtype=torch.float16, device=dev)
+    for _ in range(3):
+        torch.matmul(ga, gb)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        torch.matmul(ga, gb)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2 * 8192 ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del ga, gb
 
     # ---- saved activations: ours (O + lse) vs a materialised-scores path (P kept for backward)
     B, N, L, H, D = cfg.shape
@@ -375,19 +520,26 @@ def main():
         },
         "pct_mfma_peak": round(100 * tf_step / PEAK_MFMA_TFLOPS, 2),
         "timing": "K steps launched through the C ABI between two events on the stream, inputs resident; "
-                  "a HIP-graph replay of the same step is reported as ms_per_step_graph",
+                  "a HIP-graph replay of the same step is reported as ms_per_step_graph; per-call warm and "
+                  "cold (1 GiB written between calls) medians and minima under calls",
         "ms_per_step_graph": round(ms_graph, 5),
         "fwd": {"ms": round(ms_fwd, 5), "tflops": round(tf_fwd, 2), "pct_peak": round(100 * tf_fwd / PEAK_MFMA_TFLOPS, 2)},
+        "bwd": {"ms": round(ms_bwd, 5), "tflops": round(tf_bwd, 2), "pct_peak": round(100 * tf_bwd / PEAK_MFMA_TFLOPS, 2)},
+        "calls": calls,
         "fwd_inference": {"ms": round(ms_fwd_inf, 5), "tflops": round(tf_fwd * ms_fwd / ms_fwd_inf, 2),
                           "note": "forward with no lse kept (no backward follows)"},
         "step_transposed_layout": {"ms": round(ms_step_t, 5), "tflops": round(tf_step * ms_step / ms_step_t, 2),
                                    "note": "fwd+bwd on Q, K, V, dO views transposed over N and L (no copy)"},
         "padded_batch_uniform": pad_uniform,
         "padded_batch_mixed": pad_mixed,
-        "bwd": {"ms": round(ms_bwd, 5), "tflops": round(tf_bwd, 2), "pct_peak": round(100 * tf_bwd / PEAK_MFMA_TFLOPS, 2)},
         "kernels": {n: {"avg_us": round(v_["avg_us"], 2), "launches": v_["launches"], "share": round(v_["share"], 3)}
                     for n, v_ in kernels.items()},
         "roofline": roofline,
+        "roofline_fwd_bwd": wholes,
+        "per_config": per_config,
+        "gemm_reference": {"tflops": round(gemm_tflops, 1),
+                           "what": "torch.matmul fp16 8192^3 on the same device (library GEMM), next to the "
+                                   f"{PEAK_MFMA_TFLOPS} TFLOP/s spec peak"},
         "memory": {"saved_bytes_ours": ours_saved, "saved_bytes_materialised": mat_saved,
                    "fwd_peak_bytes_ours": int(ours_peak), "fwd_peak_bytes_materialised": int(mat_peak),
                    "ratio_saved": round(mat_saved / ours_saved, 2)},
