@@ -38,6 +38,28 @@ constexpr int kFwdWaves = 4;
 constexpr int kFwdRows = 32 * kFwdWaves;  // query rows per workgroup
 constexpr float kTauNat = 5.545177444479562f;  // 8 * ln 2
 
+// Key tiles of the forward without a pair bias at D <= 32: 128 keys (256 at
+// D = 8, where a row is 16 bytes), half the LDS of the shared tile, so that
+// three 4-wave workgroups (three waves per SIMD, at most 168 VGPRs each) share
+// a CU (measured on MI355X: -13% at (1,384,512,8,32)).  With a pair bias the
+// resident bias registers do not fit that budget, nor does D = 64: those keep
+// the shared tile at two waves per SIMD.
+template <int D>
+struct FwdTileNoPair {
+  static constexpr int CH = (D == 8) ? 256 : 128;
+  static constexpr int KC = D / 8;
+  static constexpr int VC = (D < 32 ? 32 : D) / 8;
+  static constexpr int KCH = CH * KC;
+  static constexpr int VCH = CH * VC;
+  static constexpr int TCH = KCH + VCH;
+  static constexpr int BUF_BYTES = TCH * 16;
+  static_assert(TCH % 256 == 0, "tile must split evenly over 256 threads");
+};
+template <int D, bool HAS_PAIR>
+constexpr bool kFwdThreeWaves = !HAS_PAIR && D <= 32;
+template <int D, bool HAS_PAIR>
+using FwdTile = typename std::conditional<kFwdThreeWaves<D, HAS_PAIR>, FwdTileNoPair<D>, KVTile<D>>::type;
+
 template <int D>
 struct FwdShape {
   static constexpr int KSTEPS_D = (D + 15) / 16;  // 16-wide k-steps over d (zero past D)
@@ -74,9 +96,10 @@ __device__ __forceinline__ uint16_t pick16(const u32x2 (&b)[4], int r) {
 }
 
 template <class T, int D, bool HAS_MASK, bool HAS_PAIR, int RES>
-__global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void evo_fwd_kernel(FwdArgs a) {
   using S = FwdShape<D>;
-  using TL = KVTile<D>;
+  using TL = FwdTile<D, HAS_PAIR>;
+  constexpr int kMcBufs = (std::is_same<T, F16>::value && D <= 32) ? 2 : 1;
   // two K/V tile buffers; with a resident pair bias the same bytes first hold
   // the workgroup's 128 x (32 RES) bias slab
   constexpr int kSlab = RES > 0 ? kFwdRows * RES * 64 : 0;
@@ -282,6 +305,21 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       }
     }
   };
+  // The same, issued as reads the compiler does not track (it otherwise waits
+  // for every LDS read in flight, the K prefetch included, before them); used
+  // for the prefetch two blocks ahead and completed by the wait before the PV
+  // product.  maddr is the LDS address of smk[buf][4 half].
+  auto mc_fetch_async = [&](auto jbc, const uint32_t maddr, floatx16& dst) {
+    if constexpr (HAS_MASK) {
+      constexpr int jb = decltype(jbc)::value;
+      static_for<0, 4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        const floatx4 v = __builtin_bit_cast(floatx4, lds_b128_imm<(jb * 32 + 8 * q) * 4>(maddr));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[4 * q + e] = v[e];
+      });
+    }
+  };
   // ---- S^T block = K Q^T + sqrt(D) mask for 32 keys
   auto qk_block = [&](const short8_t (&kop_in)[S::KSTEPS_D], const floatx16& minit) -> floatx16 {
     floatx16 acc = HAS_MASK ? minit : floatx16{};
@@ -300,7 +338,11 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
     if constexpr (jb_pre >= 0) {
       if (pre_live) {
         k_fetch(prec, bufa, kpre);
-        mc_fetch(tb, jb_pre, mpre);
+        if constexpr (kMcBufs == 2) {
+          mc_fetch_async(prec, lds_addr(&smk[tb][4 * half]), mpre);
+        } else {
+          mc_fetch(tb, jb_pre, mpre);
+        }
       }
     }
     short4_t vt[4 * S::MB];  // [t][mb][lo/hi]
@@ -374,6 +416,7 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
       }
     }
     lds_wait_all(vt, kpre);
+    if constexpr (kMcBufs == 2) reg_touch(mpre);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const short8_t bop = __builtin_bit_cast(short8_t, u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]});
@@ -437,34 +480,42 @@ __global__ __launch_bounds__(256, 2) void evo_fwd_kernel(FwdArgs a) {
     {
       constexpr int NB = (RES > 0 && RES < TL::CH / 32) ? RES : TL::CH / 32;
       short8_t kreg[2][S::KSTEPS_D];
-      floatx16 sacc[2], mc0 = {}, mc = {};
+      // fp16 with D <= 32: the mask term of block j sits in mcb[j & 1], so the prefetch for
+      // block j + 2 never writes the registers the QK^T product just issued for
+      // block j + 1 still reads as its accumulator input, and it is issued
+      // untracked (the compiler does not then wait for the K prefetch before
+      // it: -3% at (1,256,256,4,32)).  bf16 and D = 64, whose kernels are at
+      // the register limit: block 0 in mcb[0] and every later block in mcb[1],
+      // loaded by tracked reads.
+      floatx16 sacc[2], mcb[2] = {floatx16{}, floatx16{}};
+      auto msel = [](int j) { return kMcBufs == 2 ? (j & 1) : (j == 0 ? 0 : 1); };
       const uint32_t bufa = lds_addr(buf);
       k_fetch(std::integral_constant<int, 0>{}, bufa, kreg[0]);
-      mc_fetch(tb, 0, mc0);
+      mc_fetch(tb, 0, mcb[0]);
       if (nblk > 1) {
         k_fetch(std::integral_constant<int, 1>{}, bufa, kreg[1]);
-        mc_fetch(tb, 1, mc);
+        mc_fetch(tb, 1, mcb[1]);
       }
       {
         short4_t none[2] = {};
         lds_wait_all(none, kreg[0]);
         lds_wait_all(none, kreg[1]);
       }
-      sacc[0] = qk_block(kreg[0], mc0);
+      sacc[0] = qk_block(kreg[0], mcb[0]);
       static_for<0, NB>([&](auto jbc) {
         constexpr int jb = decltype(jbc)::value;
         if (jb < nblk) {
           if constexpr (jb + 1 < NB) {
-            if (jb + 1 < nblk) sacc[(jb + 1) & 1] = qk_block(kreg[(jb + 1) & 1], mc);
+            if (jb + 1 < nblk) sacc[(jb + 1) & 1] = qk_block(kreg[(jb + 1) & 1], mcb[msel(jb + 1)]);
           }
           // the K operands of block jb + 2 are read only when it exists
           const bool pre_live = jb + 2 < nblk;
           constexpr int jpre = jb + 2 < NB ? jb + 2 : -1;
           if constexpr (RES > 0) {
-            softmax_pv(sacc[jb & 1], tb, jbc, pres[jb < RES ? jb : 0], kreg[jb & 1], mc,
+            softmax_pv(sacc[jb & 1], tb, jbc, pres[jb < RES ? jb : 0], kreg[jb & 1], mcb[msel(jb + 2)],
                        std::integral_constant<int, jpre>{}, pre_live);
           } else {
-            softmax_pv(sacc[jb & 1], tb, jbc, ptile[HAS_PAIR ? jb : 0], kreg[jb & 1], mc,
+            softmax_pv(sacc[jb & 1], tb, jbc, ptile[HAS_PAIR ? jb : 0], kreg[jb & 1], mcb[msel(jb + 2)],
                        std::integral_constant<int, jpre>{}, pre_live);
           }
         }
