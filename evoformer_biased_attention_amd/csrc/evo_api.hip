@@ -203,7 +203,7 @@ int64_t key_tile(int64_t D) { return D == 64 ? 128 : 256; }
 // (256 CUs).  The group count k is the smallest within 3% of the minimum of
 // (rounds of workgroups) x (slices per workgroup): fewer groups mean fewer
 // dpair partials and fewer per-workgroup set-ups.
-int plan_bwdq_group(const Shape& s) {
+int plan_bwdq_group(const Shape& s, bool has_pair) {
   const int64_t jtiles = (s.L + key_tile(s.D) - 1) / key_tile(s.D);
   const int64_t per_group = s.B * s.H * ((s.L + 127) / 128) * jtiles;
   const int64_t kmax = s.N < 4096 ? s.N : 4096;
@@ -212,7 +212,12 @@ int plan_bwdq_group(const Shape& s) {
   for (int64_t k = 1; k <= kmax; ++k) best_t = std::min(best_t, cost(k));
   int64_t k = 1;
   while (k < kmax && cost(k) * 100 > best_t * 103) ++k;
-  return (int)((s.N + k - 1) / k);
+  int64_t g = (s.N + k - 1) / k;
+  // rows longer than one key tile without a pair bias (no dpair partials to
+  // multiply): groups of at most 24 slices run in more, shorter rounds
+  // (measured on MI355X at (1,384,512,8,32): 374 -> 351 us)
+  if (jtiles > 1 && !has_pair && g > 24) g = 24;
+  return (int)g;
 }
 
 // slices per bwd_kv3 workgroup: same rule over the key-side grid (one
@@ -225,7 +230,12 @@ int plan_bwdkv_group(const Shape& s) {
   for (int64_t k = 1; k <= kmax; ++k) best_t = std::min(best_t, cost(k));
   int64_t k = 1;
   while (k < kmax && cost(k) * 100 > best_t * 103) ++k;
-  return (int)((s.N + k - 1) / k);
+  int64_t g = (s.N + k - 1) / k;
+  // rows longer than one key tile (the query tiles walked per slice): groups
+  // of at most 8 slices (measured on MI355X: 383 -> 357 us at (1,384,512,8,32),
+  // 1287 -> 1174 us at (1,768,768,4,32); rows of one tile keep the rule above)
+  if (s.L > key_tile(s.D) && g > 8) g = 8;
+  return (int)g;
 }
 
 struct WsLayout {
@@ -237,7 +247,7 @@ WsLayout ws_layout(const Shape& s, bool has_mask, bool has_pair) {
   WsLayout w;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows = (size_t)s.B * s.N * s.H * s.L * sizeof(float);
-  w.gq = plan_bwdq_group(s);
+  w.gq = plan_bwdq_group(s, has_pair);
   w.ngq = (int)((s.N + w.gq - 1) / w.gq);
   size_t off = 0;
   w.delta = off;

@@ -418,11 +418,14 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
             dpacc[2 * st + 1] = T::mfma16k16(ident, __builtin_bit_cast(short4_t, u32x2{dw[2], dw[3]}), dpacc[2 * st + 1]);
           }
         }
-        lgkm_wait<0>();
+        // the transposed and prefetch reads complete here, after the vector
+        // work (the packed dS is an operand of the wait)
+        short8_t dsw = dsb;
+        lgkm_wait_after(dsw);
 #pragma unroll
         for (int k = 0; k < 2 * MB; ++k) reg_touch(kt[k]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) dq[mb] = T::mfma16(cat4(kt[2 * mb], kt[2 * mb + 1]), dsb, dq[mb]);
+        for (int mb = 0; mb < MB; ++mb) dq[mb] = T::mfma16(cat4(kt[2 * mb], kt[2 * mb + 1]), dsw, dq[mb]);
       }
     });
     vm_wait_all();  // the next slice's copies and row loads
@@ -823,13 +826,16 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
               dmk = T::mfma16(ones, db, dmk);
             }
           }
-          lgkm_wait<0>();
+          // the transposed and prefetch reads complete here, after the vector
+          // work (the packed P and dS are operands of the wait)
+          short8_t pbw = pb, dbw = db;
+          lgkm_wait_after(pbw, dbw);
 #pragma unroll
           for (int k = 0; k < 4 * MB; ++k) reg_touch(tt[k]);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            dk[mb] = T::mfma16(cat4(tt[4 * mb], tt[4 * mb + 1]), db, dk[mb]);
-            dv[mb] = T::mfma16(cat4(tt[4 * mb + 2], tt[4 * mb + 3]), pb, dv[mb]);
+            dk[mb] = T::mfma16(cat4(tt[4 * mb], tt[4 * mb + 1]), dbw, dk[mb]);
+            dv[mb] = T::mfma16(cat4(tt[4 * mb + 2], tt[4 * mb + 3]), pbw, dv[mb]);
           }
         }
       });

@@ -276,6 +276,20 @@ __device__ __forceinline__ void lds_wait_all(short4_t (&r)[N]) {
   }
 }
 
+// Wait for every LDS read in flight, placed after the instructions that
+// produce `a` (and `b`): they are operands of the wait, so the scheduler
+// cannot hoist it above them.  A wait with only a memory clobber may be
+// scheduled above plain ALU work, which then stalls on reads issued just
+// before it instead of covering their latency.
+template <class A>
+__device__ __forceinline__ void lgkm_wait_after(A& a) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a)::"memory");
+}
+template <class A, class B>
+__device__ __forceinline__ void lgkm_wait_after(A& a, B& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b)::"memory");
+}
+
 // Row stride (in 16-bit elements) for an LDS tile whose rows are read 16 bytes
 // per lane, one row per lane: a multiple of 4 dwords with an odd multiplier,
 // so 16 consecutive rows land on distinct bank quads.

@@ -415,14 +415,21 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
         l_part = T::rowsum_add(l_part, p0, p1, pk[rr / 2]);
       }
     }
-    lds_wait_all(vt, kpre);
+    // the V^T and prefetch reads complete here, after the exps (the packed
+    // probabilities are operands of the wait)
+    u32x4 bop[2] = {u32x4{pk[0], pk[1], pk[2], pk[3]}, u32x4{pk[4], pk[5], pk[6], pk[7]}};
+    lgkm_wait_after(bop[0], bop[1]);
+#pragma unroll
+    for (int k = 0; k < 4 * S::MB; ++k) reg_touch(vt[k]);
+#pragma unroll
+    for (int k = 0; k < S::KSTEPS_D; ++k) reg_touch(kpre[k]);
     if constexpr (kMcBufs == 2) reg_touch(mpre);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const short8_t bop = __builtin_bit_cast(short8_t, u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]});
 #pragma unroll
       for (int mb2 = 0; mb2 < S::MB; ++mb2)
-        oacc[mb2] = T::mfma(cat4(vt[(t * S::MB + mb2) * 2], vt[(t * S::MB + mb2) * 2 + 1]), bop, oacc[mb2]);
+        oacc[mb2] = T::mfma(cat4(vt[(t * S::MB + mb2) * 2], vt[(t * S::MB + mb2) * 2 + 1]),
+                            __builtin_bit_cast(short8_t, bop[t]), oacc[mb2]);
     }
   };
 
