@@ -37,6 +37,7 @@ namespace evo {
 constexpr int kFwdWaves = 4;
 constexpr int kFwdRows = 32 * kFwdWaves;  // query rows per workgroup
 constexpr float kTauNat = 5.545177444479562f;  // 8 * ln 2
+constexpr float kFastSum = 256.f;  // 2^8: a block sum below it keeps the exponent base (no block max)
 
 // Key tiles of the forward without a pair bias at D <= 32: 128 keys (256 at
 // D = 8, where a row is 16 bytes), half the LDS of the shared tile, so that
@@ -100,6 +101,10 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
   using S = FwdShape<D>;
   using TL = FwdTile<D, HAS_PAIR>;
   constexpr int kMcBufs = (std::is_same<T, F16>::value && D <= 32) ? 2 : 1;
+  // the block max only when needed (A/B on one MI355X: (1,384,512,8,32) bf16
+  // forward -1.6%, the other shapes within the noise); not for bf16 with a
+  // resident pair bias, where its extra registers spill (+5% at (1,512,256,8,8))
+  constexpr bool kSkipMax = !(std::is_same<T, BF16>::value && RES > 0);
   // two K/V tile buffers; with a resident pair bias the same bytes first hold
   // the workgroup's 128 x (32 RES) bias slab
   constexpr int kSlab = RES > 0 ? kFwdRows * RES * 64 : 0;
@@ -367,53 +372,137 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) sv[rr] = acc[rr] * a.scale;
     }
-    // block max in two chains of three-input maxima (half the dependency depth
-    // of one chain).  Written as assembly: the scores come out of assembly
-    // (v_fma_mix_f32), so the compiler would first canonicalize them for its
-    // own maximum (four extra instructions per block); scores are never NaN
-    // for finite inputs.
-    auto max3 = [](float x, float y, float z) {
-      float r;
-      asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
-      return r;
-    };
-    float mb0 = max3(sv[0], sv[1], sv[2]), mb1 = max3(sv[8], sv[9], sv[10]);
-    mb0 = max3(mb0, sv[3], sv[4]);
-    mb1 = max3(mb1, sv[11], sv[12]);
-    mb0 = max3(mb0, sv[5], sv[6]);
-    mb1 = max3(mb1, sv[13], sv[14]);
-    mb0 = max3(mb0, mb1, sv[7]);
-    float mb = max3(mb0, sv[15], sv[15]);
-    {  // with the partner half (lane ^ 32) holding the same query row
-      float pa = mb, pb = mb;
-      xhalf_swap(pa, pb);
-      mb = max3(pa, pb, pb);
-    }
-    const bool need = mb > m_used + kTauNat;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_new = need ? mb : m_used;
-      const float alpha = need ? __builtin_amdgcn_exp2f((m_used - m_new) * kLog2e) : 1.f;
-      m_used = m_new;
-      l_part *= alpha;
-      l_part2 *= alpha;
-#pragma unroll
-      for (int mb2 = 0; mb2 < S::MB; ++mb2)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) oacc[mb2][rr] *= alpha;
-    }
-    const float neg_ml = (m_used == kNegInf) ? 0.f : -m_used * kLog2e;
+    // The exponent base moves only when it has to (the base may lag the row
+    // max by up to 8 in log2 units; exp values stay below 2^8 that way).
     uint32_t pk[8];
+    if constexpr (kSkipMax) {
+      // The exps are first taken against the current base m_used: if a row's
+      // block sum stays below 2^8 in both halves, each of its probabilities
+      // does, so no score lies more than 8 (log2 units) above the base and the
+      // max-first rule would keep the base too: the row's block is done
+      // without its maximum.  Otherwise (or on the first block of a row, whose
+      // base is still -inf) the block max is formed and the row's base moved to
+      // it when it exceeds the old one by more than 8 (log2 units), rescaling
+      // the O^T accumulator and the row sums, and the exps are taken again.
+      // Both rules give the same base and the same sums (up to the rounding of
+      // the comparison itself), so the two kernels agree bit for bit.
+      float bs0, bs1;  // block sums, two chains
+      auto exps = [&](const float neg_ml) {
+        bs0 = 0.f;
+        bs1 = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 16; rr += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr], kLog2e, neg_ml));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr + 1], kLog2e, neg_ml));
-      pk[rr / 2] = T::pack2(p0, p1);
-      // fp16: two chains of v_dot2; bf16 sums in fp32 (its register budget is tighter)
-      if (std::is_same<T, F16>::value && ((rr / 2) & 1)) {
-        l_part2 = T::rowsum_add(l_part2, p0, p1, pk[rr / 2]);
-      } else {
-        l_part = T::rowsum_add(l_part, p0, p1, pk[rr / 2]);
+        for (int rr = 0; rr < 16; rr += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr], kLog2e, neg_ml));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr + 1], kLog2e, neg_ml));
+          pk[rr / 2] = T::pack2(p0, p1);
+          // fp16: the rounded pair by v_dot2; bf16 sums the fp32 values
+          if ((rr / 2) & 1) {
+            bs1 = T::rowsum_add(bs1, p0, p1, pk[rr / 2]);
+          } else {
+            bs0 = T::rowsum_add(bs0, p0, p1, pk[rr / 2]);
+          }
+        }
+      };
+      // The choice is made per query row (the lane and its partner half), so a
+      // row's bits never depend on the other rows of the wave.
+      const bool first = m_used == kNegInf;
+      bool redo = first;
+      if (__builtin_amdgcn_ballot_w64(!first) != 0) {
+        exps(first ? 0.f : -m_used * kLog2e);
+        redo = first || !(bs0 + bs1 < kFastSum);
       }
+      if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+        {  // the row redoes when either half of it does
+          float fa = redo ? 1.f : 0.f, fb = fa;
+          xhalf_swap(fa, fb);
+          redo = (fa + fb) > 0.f;
+        }
+        // block max in two chains of three-input maxima.  Written as assembly:
+        // the scores come out of assembly (v_fma_mix_f32), so the compiler would
+        // first canonicalize them for its own maximum; scores are never NaN for
+        // finite inputs.
+        auto max3 = [](float x, float y, float z) {
+          float r;
+          asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+          return r;
+        };
+        float mb0 = max3(sv[0], sv[1], sv[2]), mb1 = max3(sv[8], sv[9], sv[10]);
+        mb0 = max3(mb0, sv[3], sv[4]);
+        mb1 = max3(mb1, sv[11], sv[12]);
+        mb0 = max3(mb0, sv[5], sv[6]);
+        mb1 = max3(mb1, sv[13], sv[14]);
+        mb0 = max3(mb0, mb1, sv[7]);
+        float mb = max3(mb0, sv[15], sv[15]);
+        {  // with the partner half (lane ^ 32) holding the same query row
+          float pa = mb, pb = mb;
+          xhalf_swap(pa, pb);
+          mb = max3(pa, pb, pb);
+        }
+        // rows that keep their base recompute the same exps
+        const bool need = redo && mb > m_used + kTauNat;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          const float m_new = need ? mb : m_used;
+          const float alpha = need ? __builtin_amdgcn_exp2f((m_used - m_new) * kLog2e) : 1.f;
+          m_used = m_new;
+          l_part *= alpha;
+          l_part2 *= alpha;
+#pragma unroll
+          for (int mb2 = 0; mb2 < S::MB; ++mb2)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) oacc[mb2][rr] *= alpha;
+        }
+        exps((m_used == kNegInf) ? 0.f : -m_used * kLog2e);
+      }
+      l_part += bs0;
+      l_part2 += bs1;
+
+    } else {
+      // bf16 with a resident pair bias (at the register limit): the block max
+      // first, then the exps
+      auto max3 = [](float x, float y, float z) {
+        float r;
+        asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+        return r;
+      };
+      float mb0 = max3(sv[0], sv[1], sv[2]), mb1 = max3(sv[8], sv[9], sv[10]);
+      mb0 = max3(mb0, sv[3], sv[4]);
+      mb1 = max3(mb1, sv[11], sv[12]);
+      mb0 = max3(mb0, sv[5], sv[6]);
+      mb1 = max3(mb1, sv[13], sv[14]);
+      mb0 = max3(mb0, mb1, sv[7]);
+      float mb = max3(mb0, sv[15], sv[15]);
+      {
+        float pa = mb, pb = mb;
+        xhalf_swap(pa, pb);
+        mb = max3(pa, pb, pb);
+      }
+      const bool need = mb > m_used + kTauNat;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? mb : m_used;
+        const float alpha = need ? __builtin_amdgcn_exp2f((m_used - m_new) * kLog2e) : 1.f;
+        m_used = m_new;
+        l_part *= alpha;
+        l_part2 *= alpha;
+#pragma unroll
+        for (int mb2 = 0; mb2 < S::MB; ++mb2)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) oacc[mb2][rr] *= alpha;
+      }
+      const float neg_ml = (m_used == kNegInf) ? 0.f : -m_used * kLog2e;
+      float bs0 = 0.f, bs1 = 0.f;  // summed as the other branch sums
+#pragma unroll
+      for (int rr = 0; rr < 16; rr += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr], kLog2e, neg_ml));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr + 1], kLog2e, neg_ml));
+        pk[rr / 2] = T::pack2(p0, p1);
+        if ((rr / 2) & 1) {
+          bs1 = T::rowsum_add(bs1, p0, p1, pk[rr / 2]);
+        } else {
+          bs0 = T::rowsum_add(bs0, p0, p1, pk[rr / 2]);
+        }
+      }
+      l_part += bs0;
+      l_part2 += bs1;
     }
     // the V^T and prefetch reads complete here, after the exps (the packed
     // probabilities are operands of the wait)
