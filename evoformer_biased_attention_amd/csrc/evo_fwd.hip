@@ -222,8 +222,15 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
   // issue the asynchronous copy of tile t into LDS buffer (t & 1): a uniform
   // base pointer (the tile's first key row of the slice) plus a 32-bit byte
   // offset per 16-byte chunk (K-layout chunks, then V-layout chunks; rows past
-  // L clamp to L - 1), so the copies address by scalar base + vector offset
+  // L clamp to L - 1), so the copies address by scalar base + vector offset.
+  // A thread's copy blocks of 64 chunks start on multiples of 64 chunks, so
+  // with C chunks per row (C divides 64) a lane's row within its block is
+  // lane / C, its chunk lane % C, and its row's swizzle (period 16 rows; the
+  // blocks' first rows differ by multiples of 16) the same in every block of a
+  // kind: each copy adds only its block's first row, a wave-uniform offset.
   constexpr int NCH = TL::TCH / 256;  // chunks per thread
+  static_assert(TL::KCH % 256 == 0, "K chunks must fill whole copy rounds");
+  static_assert(64 % TL::KC == 0 && 64 % TL::VC == 0, "a copy block must hold whole rows");
   const uint32_t sl2 = (uint32_t)a.sL * 2u, hd2 = (uint32_t)(h * D) * 2u;
   auto issue_tile = [&](int t) {
     const int c = t % nchunks;
@@ -233,28 +240,44 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
     const char* kbase = reinterpret_cast<const char*>(a.k + row0);
     const char* vbase = reinterpret_cast<const char*>(a.v + row0);
     uint8_t* buf = smem + (t & 1) * TL::BUF_BYTES;
-    // the offsets are recomputed per tile (a few integer ops per chunk) rather
-    // than kept in registers across the tile loop
-    int ln = lane;
+    const bool full = lim == TL::CH - 1;  // no row of the tile lies past L
+    // the two per-lane offsets are recomputed per tile (a dozen integer ops)
+    // rather than kept in registers across the tile loop
+    uint32_t ln = (uint32_t)lane;  // unsigned: the divisions below are shifts
     asm volatile("" : "+v"(ln));
+    uint32_t kv_lane[2];  // per-lane byte offset within a copy block: K, V
+    {
+      const int rk = (int)(ln / TL::KC), rv = (int)(ln / TL::VC);
+      const int ck = (int)(ln % TL::KC) ^ kv_swz<TL::KC>(wave_u * 64 / TL::KC + rk);
+      int cv = (int)(ln % TL::VC) ^ kv_swz<TL::VC>(wave_u * 64 / TL::VC + rv);
+      if (cv >= D / 8) cv = 0;  // columns the transposed reads touch but never use
+      kv_lane[0] = (uint32_t)rk * sl2 + hd2 + 16u * (uint32_t)ck;
+      kv_lane[1] = (uint32_t)rv * sl2 + hd2 + 16u * (uint32_t)cv;
+    }
+    constexpr int kRounds = TL::KCH / 256;  // K chunks fill the first rounds
+    auto copy = [&](auto full_c) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int base = wave_u * 64 + 256 * i;  // wave-uniform
-      const int q = base + ln;
-      int r, cc;
-      if (base < TL::KCH) {
-        r = q / TL::KC;
-        cc = (q % TL::KC) ^ kv_swz<TL::KC>(r);
-      } else {
-        const int q2 = q - TL::KCH;
-        r = q2 / TL::VC;
-        cc = (q2 % TL::VC) ^ kv_swz<TL::VC>(r);
-        if (cc >= D / 8) cc = 0;  // columns the transposed reads touch but never use
+      for (int i = 0; i < NCH; ++i) {
+        const bool is_k = i < kRounds;
+        const int base = wave_u * 64 + 256 * i;  // wave-uniform
+        const int rb = is_k ? base / TL::KC : (base - TL::KCH) / TL::VC;  // block's first row
+        uint32_t off;
+        if constexpr (decltype(full_c)::value) {
+          off = (uint32_t)rb * sl2 + kv_lane[is_k ? 0 : 1];
+        } else {
+          const int lrow = (int)(is_k ? ln / TL::KC : ln / TL::VC);
+          const uint32_t lcol = kv_lane[is_k ? 0 : 1] - (uint32_t)lrow * sl2;
+          off = (uint32_t)min(rb + lrow, lim) * sl2 + lcol;
+        }
+        const char* src = (is_k ? kbase : vbase) + off;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(buf + base * 16), 16, 0, 0);
       }
-      const uint32_t off = (uint32_t)min(r, lim) * sl2 + hd2 + 16u * (uint32_t)cc;
-      const char* src = (base < TL::KCH ? kbase : vbase) + off;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(buf + base * 16), 16, 0, 0);
+    };
+    if (full) {
+      copy(std::true_type{});
+    } else {
+      copy(std::false_type{});
     }
   };
 
