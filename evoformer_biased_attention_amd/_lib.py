@@ -38,6 +38,7 @@ EXPORTED = (
     "evo_attn_bwd_strided",
     "evo_attn_bwd_noalloc",
     "evo_attn_bwd_workspace_bytes",
+    "evo_attn_bwd_workspace_bytes_within",
     "evo_attn_bwd_workspace_offsets",
     "evo_status_string",
     "evo_attn_profile_enable",
@@ -77,6 +78,8 @@ def load() -> ctypes.CDLL:
     lib.evo_attn_bwd_noalloc.restype = I
     lib.evo_attn_bwd_workspace_bytes.argtypes = [S, I, I, I]
     lib.evo_attn_bwd_workspace_bytes.restype = Z
+    lib.evo_attn_bwd_workspace_bytes_within.argtypes = [S, I, I, I, Z]
+    lib.evo_attn_bwd_workspace_bytes_within.restype = Z
     lib.evo_attn_bwd_workspace_offsets.argtypes = [S, I, I, I, ctypes.POINTER(Z), ctypes.POINTER(Z), ctypes.POINTER(Z)]
     lib.evo_attn_bwd_workspace_offsets.restype = I
     lib.evo_status_string.argtypes = [I]
@@ -134,6 +137,11 @@ def evo_attn_bwd_noalloc(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, 
 
 def evo_attn_bwd_workspace_bytes(shape, dtype, has_mask, has_pair) -> int:
     return int(load().evo_attn_bwd_workspace_bytes(shape_arg(shape), dtype, int(has_mask), int(has_pair)))
+
+
+def evo_attn_bwd_workspace_bytes_within(shape, dtype, has_mask, has_pair, partial_budget) -> int:
+    return int(load().evo_attn_bwd_workspace_bytes_within(shape_arg(shape), dtype, int(has_mask), int(has_pair),
+                                                          int(partial_budget)))
 
 
 def evo_attn_bwd_workspace_offsets(shape, dtype, has_mask, has_pair):

@@ -112,8 +112,14 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_bias: Optio
 
 
 def attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask: bool = True, want_dpair: bool = True,
-             workspace: Optional[torch.Tensor] = None) -> Dict[str, Optional[torch.Tensor]]:
-    """Backward: returns dict dq, dk, dv, dmask (or None), dpair (or None), workspace."""
+             workspace: Optional[torch.Tensor] = None,
+             partial_budget: Optional[int] = None) -> Dict[str, Optional[torch.Tensor]]:
+    """Backward: returns dict dq, dk, dv, dmask (or None), dpair (or None), workspace.
+
+    The library fits its plan to the workspace: a given `workspace` is used as
+    it is (it must hold at least the least workspace the backward accepts);
+    otherwise one is allocated, of the default size or of the size for
+    `partial_budget` bytes of fp32 partials (long rows then go in chunks)."""
     _check_inputs(q, k, v, mask_bias, pair_bias)
     lay = _layout((q, k, v, out))
     if lay is None:
@@ -130,9 +136,15 @@ def attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask: bool = T
     dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) for _ in range(3))
     dmask = torch.empty_like(mask_bias) if (mask_bias is not None and want_dmask) else None
     dpair = torch.empty_like(pair_bias) if (pair_bias is not None and want_dpair) else None
-    nbytes = _lib.evo_attn_bwd_workspace_bytes(q.shape, dt, mask_bias is not None, pair_bias is not None)
-    if workspace is None or workspace.numel() < nbytes:
+    hm, hp = mask_bias is not None, pair_bias is not None
+    if workspace is None:
+        if partial_budget is None:
+            nbytes = _lib.evo_attn_bwd_workspace_bytes(q.shape, dt, hm, hp)
+        else:
+            nbytes = _lib.evo_attn_bwd_workspace_bytes_within(q.shape, dt, hm, hp, partial_budget)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() < _lib.evo_attn_bwd_workspace_bytes_within(q.shape, dt, hm, hp, 0):
+        raise ValueError("workspace smaller than the least the backward accepts")
     _lib.check(_lib.evo_attn_bwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), _ptr(mask_bias),
                                          _ptr(pair_bias), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(dmask), _ptr(dpair),

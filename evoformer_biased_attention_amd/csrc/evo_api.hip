@@ -13,6 +13,7 @@
 #include <climits>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "../../include/evo_attn.h"
 #include "evo_kernels.h"
@@ -238,44 +239,115 @@ int plan_bwdkv_group(const Shape& s) {
   return (int)g;
 }
 
+// bwd_q3 plan: slices per workgroup (gq), workgroups per (b, h, query tile,
+// key tile) in a chunk (ngq, also the dpair group slots) and slices per chunk
+// (nc).  Rows of one key tile take all slices at once (no dQ partials).
+// Longer rows keep their fp32 partials (dQ per key tile of the chunk's slices,
+// plus the dpair slots) within a byte budget: the one-chunk plan when it fits,
+// else, of the chunkings and group counts that fit, the first in a fixed order
+// (modelled time: chunks x workgroup rounds x (slices per workgroup + 4, the
+// set-up of a workgroup in slice units); then fewer chunks, then fewer
+// groups), else one slice at a time (the least workspace the backward can run
+// in).  The order does not depend on the budget, so a plan chosen for one
+// budget is chosen again for any smaller budget it still fits.
+struct BwdQPlan {
+  int gq, ngq, nc;
+};
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+BwdQPlan plan_bwdq(const Shape& s, bool has_pair, size_t budget) {
+  const int64_t jtiles = (s.L + key_tile(s.D) - 1) / key_tile(s.D);
+  const int64_t g1 = plan_bwdq_group(s, has_pair);
+  const int64_t k1 = (s.N + g1 - 1) / g1;
+  if (jtiles == 1) return {(int)g1, (int)k1, (int)s.N};
+  const size_t dq_slice = (size_t)jtiles * s.B * s.L * s.H * s.D * sizeof(float);
+  const size_t slot = has_pair ? (size_t)s.B * s.H * s.L * s.L * sizeof(float) : 0;
+  auto bytes = [&](int64_t nc, int64_t k) { return al256((size_t)nc * dq_slice) + al256((size_t)k * slot); };
+  if (bytes(s.N, k1) <= budget) return {(int)g1, (int)k1, (int)s.N};
+  const int64_t per_group = s.B * s.H * ((s.L + 127) / 128) * jtiles;
+  struct Cand {
+    int64_t cost, chunks, k, g, nc;
+  };
+  std::vector<Cand> cands;
+  const int64_t cmax = std::min<int64_t>(s.N, 64);
+  for (int64_t c = 1; c <= cmax; ++c) {
+    const int64_t nc = (s.N + c - 1) / c;
+    if ((s.N + nc - 1) / nc != c) continue;  // the same chunking as a smaller count
+    for (int64_t k = 1; k <= std::min<int64_t>(nc, 64); ++k) {
+      const int64_t g = (nc + k - 1) / k;
+      if ((nc + g - 1) / g != k) continue;  // k groups of g slices do not form
+      if (!has_pair && g > 24) continue;    // as plan_bwdq_group
+      if (bytes(nc, k) > budget) continue;
+      cands.push_back({c * ((per_group * k + 255) / 256) * (g + 4), c, k, g, nc});
+    }
+  }
+  if (cands.empty()) return {1, 1, 1};
+  const Cand* pick = &cands[0];
+  for (const Cand& x : cands) {
+    if (x.cost != pick->cost ? x.cost < pick->cost
+                             : (x.chunks != pick->chunks ? x.chunks < pick->chunks : x.k < pick->k))
+      pick = &x;
+  }
+  return {(int)pick->g, (int)pick->k, (int)pick->nc};
+}
+
+// Partial budget of a workspace sized by evo_attn_bwd_workspace_bytes (A/B on
+// one MI355X, (1,768,768,4,32) bf16 step: unchunked 3.96 ms; 640 MiB +1.8%,
+// 384 MiB +3.9%, 160 MiB +12%; (1,384,512,8,32) unchanged from 384 MiB up)
+constexpr size_t kDefaultPartialBudget = (size_t)384 << 20;
+
+// Workspace: the regions whose size does not depend on the plan first (so
+// their offsets do not either), then the dpair group slots and dQ partials.
 struct WsLayout {
-  size_t delta, dmask_part, dmask_f32, dpair_part, dpair_f32, dq_part, total;
-  int gq, ngq;
+  size_t delta, dmask_part, dmask_f32, dpair_f32, fixed, dpair_part, dq_part, total;
+  int gq, ngq, nc;
 };
 
-WsLayout ws_layout(const Shape& s, bool has_mask, bool has_pair) {
+WsLayout ws_layout(const Shape& s, bool has_mask, bool has_pair, size_t budget) {
   WsLayout w;
-  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows = (size_t)s.B * s.N * s.H * s.L * sizeof(float);
-  w.gq = plan_bwdq_group(s, has_pair);
-  w.ngq = (int)((s.N + w.gq - 1) / w.gq);
+  const size_t per = (size_t)s.B * s.H * s.L * s.L * sizeof(float);
   size_t off = 0;
   w.delta = off;
-  off += al(rows);
+  off += al256(rows);
   w.dmask_part = w.dmask_f32 = (size_t)-1;
   if (has_mask) {
     w.dmask_part = off;
-    off += al(rows);
+    off += al256(rows);
     w.dmask_f32 = off;
-    off += al((size_t)s.B * s.N * s.L * sizeof(float));
+    off += al256((size_t)s.B * s.N * s.L * sizeof(float));
   }
-  w.dpair_part = w.dpair_f32 = (size_t)-1;
+  w.dpair_f32 = (size_t)-1;
   if (has_pair) {
-    const size_t per = (size_t)s.B * s.H * s.L * s.L * sizeof(float);
-    w.dpair_part = off;
-    off += al(per * (size_t)w.ngq);
     w.dpair_f32 = off;
-    off += al(per);
+    off += al256(per);
   }
-  // fp32 partials of dQ, one per key tile, when a row spans several tiles
+  w.fixed = off;
+  const BwdQPlan qp = plan_bwdq(s, has_pair, budget);
+  w.gq = qp.gq;
+  w.ngq = qp.ngq;
+  w.nc = qp.nc;
+  w.dpair_part = (size_t)-1;
+  if (has_pair) {
+    w.dpair_part = off;
+    off += al256(per * (size_t)w.ngq);
+  }
+  // fp32 partials of dQ of one chunk of slices, one per key tile, when a row
+  // spans several tiles
   w.dq_part = (size_t)-1;
   const int64_t jtiles = (s.L + key_tile(s.D) - 1) / key_tile(s.D);
   if (jtiles > 1) {
     w.dq_part = off;
-    off += al((size_t)jtiles * s.B * s.N * s.L * s.H * s.D * sizeof(float));
+    off += al256((size_t)jtiles * s.B * w.nc * s.L * s.H * s.D * sizeof(float));
   }
   w.total = off;
   return w;
+}
+
+// The layout for a workspace of `bytes`: the plan that fits what is left
+// after the fixed regions.
+WsLayout ws_layout_within(const Shape& s, bool has_mask, bool has_pair, size_t bytes) {
+  const size_t fixed = ws_layout(s, has_mask, has_pair, 0).fixed;
+  return ws_layout(s, has_mask, has_pair, bytes > fixed ? bytes - fixed : 0);
 }
 
 }  // namespace
@@ -408,7 +480,14 @@ evo_status_t evo_attn_fwd_strided(const void* q, const void* k, const void* v, c
 size_t evo_attn_bwd_workspace_bytes(const int64_t shape[5], int dtype, int has_mask, int has_pair) {
   Shape s;
   if (parse_shape(shape, dtype, &s) != EVO_OK) return 0;
-  return ws_layout(s, has_mask != 0, has_pair != 0).total;
+  return ws_layout(s, has_mask != 0, has_pair != 0, kDefaultPartialBudget).total;
+}
+
+size_t evo_attn_bwd_workspace_bytes_within(const int64_t shape[5], int dtype, int has_mask, int has_pair,
+                                           size_t partial_budget) {
+  Shape s;
+  if (parse_shape(shape, dtype, &s) != EVO_OK) return 0;
+  return ws_layout(s, has_mask != 0, has_pair != 0, partial_budget).total;
 }
 
 evo_status_t evo_attn_bwd_workspace_offsets(const int64_t shape[5], int dtype, int has_mask, int has_pair,
@@ -416,7 +495,7 @@ evo_status_t evo_attn_bwd_workspace_offsets(const int64_t shape[5], int dtype, i
   Shape s;
   evo_status_t st = parse_shape(shape, dtype, &s);
   if (st != EVO_OK) return st;
-  WsLayout w = ws_layout(s, has_mask != 0, has_pair != 0);
+  WsLayout w = ws_layout(s, has_mask != 0, has_pair != 0, 0);  // offsets do not depend on the plan
   if (off_delta) *off_delta = w.delta;
   if (off_dmask_f32) *off_dmask_f32 = w.dmask_f32;
   if (off_dpair_f32) *off_dpair_f32 = w.dpair_f32;
@@ -450,7 +529,8 @@ evo_status_t bwd_impl(const void* q, const void* k, const void* v, const void* m
   if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return EVO_ERR_NULL_POINTER;
   if ((dmask_bias && !mask_bias) || (dpair_bias && !pair_bias)) return EVO_ERR_NULL_POINTER;
   const bool has_mask = mask_bias != nullptr, has_pair = pair_bias != nullptr;
-  WsLayout w = ws_layout(s, has_mask, has_pair);
+  // the plan that fits the workspace given (the static scratch for noalloc)
+  const WsLayout w = ws_layout_within(s, has_mask, has_pair, use_scratch ? kScratchBytes : workspace_bytes);
   if (use_scratch) {
     if (w.total > kScratchBytes) return EVO_ERR_SCRATCH_LIMIT;
   } else if (!workspace || workspace_bytes < w.total) {
@@ -516,6 +596,9 @@ evo_status_t bwd_impl(const void* q, const void* k, const void* v, const void* m
   a.H = (int)s.H;
   a.Gq = w.gq;
   a.n_groups_q = w.ngq;
+  a.q_n0 = 0;
+  a.q_nc = w.nc;
+  a.dpair_carry = 0;
   a.Gk = plan_bwdkv_group(s);
   a.n_groups_k = (int)((s.N + a.Gk - 1) / a.Gk);
   a.sqrt_d = (float)std::sqrt((double)s.D);

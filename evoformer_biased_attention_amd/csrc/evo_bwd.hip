@@ -17,6 +17,13 @@
 //   bwd_fin  dmask = sum_h partials, dpair = sum_g partials, dQ = sum of the
 //            key-tile partials (rows longer than one key tile), each in a
 //            fixed order (bitwise reproducible), then rounded to dtype.
+// Rows longer than one key tile go through bwd_q3 in chunks of slices so that
+// the partials stay within a fixed budget: each chunk's dQ partials are summed
+// by a bwd_fin launch of their own, and the dpair group slots carry their sums
+// from chunk to chunk (bwd_q3 of a later chunk continues them), so the last
+// bwd_fin sums the slots once.
+#include <algorithm>
+
 #include "evo_common.h"
 #include "evo_kernels.h"
 #include "evo_prof.h"
@@ -96,9 +103,10 @@ __global__ __launch_bounds__(256) void evo_bwd_fin_kernel(BwdArgs a, int ngroups
     w[0] = T::pack2(s[0], s[1]);
     w[1] = T::pack2(s[2], s[3]);
     // the partials are dense [B,N,L,H,D]; dQ has the strides of the call
+    // (the chunk's slices q_n0 .. q_n0 + q_nc - 1)
     const int64_t hd = idx % ((int64_t)a.H * D), r = idx / ((int64_t)a.H * D);
     const int64_t l = r % a.L, bn = r / a.L;
-    const int64_t dst = (bn / a.N) * a.sB + (bn % a.N) * a.sN + l * a.sL + hd;
+    const int64_t dst = (bn / a.q_nc) * a.sB + (a.q_n0 + bn % a.q_nc) * a.sN + l * a.sL + hd;
     *reinterpret_cast<u32x2*>(a.dq + dst) = w;
   }
 }
@@ -111,30 +119,49 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   const bool want_dpair = a.dpair != nullptr;
   const bool fits = a.L <= KVTile<D>::CH;
   const int jtiles = (a.L + KVTile<D>::CH - 1) / KVTile<D>::CH;
-  if (fits) {
-    const hipError_t e = launch_bwd_tile(a, D, std::is_same<T, BF16>::value, st);
-    if (e != hipSuccess) return e;
-  } else {
-    // bwd_q3 over key tiles (dQ partials, delta, dpair partials), then
-    // bwd_kv3 over query tiles, which reads delta
-    const hipError_t e = launch_bwd_q_split(a, D, std::is_same<T, BF16>::value, st);
-    if (e != hipSuccess) return e;
-  }
   const int64_t per = (int64_t)a.B * a.H * a.L * a.L;
   const bool vec = (per % 4) == 0;
-  const int64_t n_pair = want_dpair ? (vec ? per / 4 : per) : 0;
-  const int64_t n_mask = want_dmask ? (int64_t)a.B * a.N * a.L : 0;
-  const int64_t n_dq = fits ? 0 : (int64_t)a.B * a.N * a.L * a.H * D / 4;
-  if (n_pair + n_mask + n_dq > 0) {
+  const int slots = a.n_groups_q;  // dpair group slots (those of a full chunk)
+  auto fin = [&](const BwdArgs& af, int64_t n_pair, int64_t n_mask, int64_t n_dq) {
+    if (n_pair + n_mask + n_dq == 0) return;
     const unsigned blocks = (unsigned)((n_pair + n_mask + n_dq + 255) / 256);
     prof_begin(K_BWD_FIN, st);
     if (vec)
-      hipLaunchKernelGGL((evo_bwd_fin_kernel<T, true>), dim3(blocks), dim3(256), 0, st, a, a.n_groups_q, n_pair,
-                         n_mask, n_dq, jtiles, D);
+      hipLaunchKernelGGL((evo_bwd_fin_kernel<T, true>), dim3(blocks), dim3(256), 0, st, af, slots, n_pair, n_mask,
+                         n_dq, jtiles, D);
     else
-      hipLaunchKernelGGL((evo_bwd_fin_kernel<T, false>), dim3(blocks), dim3(256), 0, st, a, a.n_groups_q, n_pair,
-                         n_mask, n_dq, jtiles, D);
+      hipLaunchKernelGGL((evo_bwd_fin_kernel<T, false>), dim3(blocks), dim3(256), 0, st, af, slots, n_pair, n_mask,
+                         n_dq, jtiles, D);
     prof_end(K_BWD_FIN, st);
+  };
+  const int64_t n_pair = want_dpair ? (vec ? per / 4 : per) : 0;
+  const int64_t n_mask = want_dmask ? (int64_t)a.B * a.N * a.L : 0;
+  const bool bf16 = std::is_same<T, BF16>::value;
+  if (fits) {
+    const hipError_t e = launch_bwd_tile(a, D, bf16, st);
+    if (e != hipSuccess) return e;
+    fin(a, n_pair, n_mask, 0);
+  } else {
+    // per chunk of slices: bwd_q3 over its key tiles (dQ partials, delta,
+    // dpair slot sums), then the sum of its dQ partials; after the last
+    // chunk bwd_kv3 over query tiles (it reads delta) and the final sums
+    const int chunks = (a.N + a.q_nc - 1) / a.q_nc;
+    for (int c = 0; c < chunks; ++c) {
+      BwdArgs ac = a;
+      ac.q_n0 = c * a.q_nc;
+      ac.q_nc = std::min(a.q_nc, a.N - ac.q_n0);
+      ac.n_groups_q = (ac.q_nc + a.Gq - 1) / a.Gq;
+      ac.dpair_carry = c > 0;
+      hipError_t e = launch_bwd_q_split(ac, D, bf16, 0, st);
+      if (e != hipSuccess) return e;
+      const int64_t n_dq = (int64_t)a.B * ac.q_nc * a.L * a.H * D / 4;
+      if (c + 1 < chunks) {
+        fin(ac, 0, 0, n_dq);
+      } else {
+        if ((e = launch_bwd_q_split(a, D, bf16, 1, st)) != hipSuccess) return e;
+        fin(ac, n_pair, n_mask, n_dq);
+      }
+    }
   }
   return hipGetLastError();
 }

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   const int i = it * kRows + wave * 16 + col;
   const bool i_valid = i < L;
   const int ic = min(i, L - 1);
-  const int n_begin = ng * a.Gq, n_end = min(N, n_begin + a.Gq);
+  const int n_begin = a.q_n0 + ng * a.Gq, n_end = min(a.q_n0 + a.q_nc, n_begin + a.Gq);
   const int ntiles = n_end - n_begin;
   const float scale = a.scale, c1 = a.scale * kLog2e;
 
@@ -211,6 +211,23 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   for (int blk = 0; blk < (WANT_DPAIR ? NB : 1); ++blk) dpacc[blk] = floatx4{0.f, 0.f, 0.f, 0.f};
   // the group's fp32 dpair partial of block blk (keys 16 blk + 4 g + 0..3 of query i)
   float* const dpdst = WANT_DPAIR ? a.dpair_part + ((((size_t)ng * a.B + b) * H + h) * L + ic) * L + kc0 : nullptr;
+  if constexpr (WANT_DPAIR) {
+    // a chunk after the first continues the sum its group slot holds (the
+    // elements store_dpair writes; the others are never stored)
+    if (a.dpair_carry && i_valid && ntiles > 0) {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        const int j = 16 * blk + 4 * g;
+        if (j + 4 <= lk && (L % 4) == 0) {
+          dpacc[blk] = *reinterpret_cast<const floatx4*>(dpdst + j);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (j + u < lk) dpacc[blk][u] = dpdst[j + u];
+        }
+      }
+    }
+  }
   auto store_dpair = [&](int blk) {
     if constexpr (WANT_DPAIR) {
       if (!i_valid) return;
@@ -435,14 +452,15 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     }
     // ---- dQ = scale * dQ^T: lane holds d = 16 mb + 4 g + 0..3 of query i
     if (i_valid) {
-      const size_t row = (((size_t)b * N + n) * L + i) * H + h;  // dense row index of the fp32 partials
+      // dense row index of the fp32 partials (slices of the chunk)
+      const size_t row = (((size_t)b * a.q_nc + (n - a.q_n0)) * L + i) * H + h;
       const int64_t qoff = b * a.sB + n * a.sN + i * a.sL + h * D;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int d = 16 * mb + 4 * g;
         if (d < D) {
           if constexpr (SPLIT) {
-            float* dst = a.dq_part + ((size_t)jt * a.B * N * L * H + row) * D + d;
+            float* dst = a.dq_part + ((size_t)jt * a.B * a.q_nc * L * H + row) * D + d;
             *reinterpret_cast<floatx4*>(dst) = dq[mb] * scale;
           } else {
             u32x2 w;
@@ -919,41 +937,45 @@ hipError_t launch_bwd_tile(const BwdArgs& a, int D, bool bf16, hipStream_t strea
 }
 
 template <class T, int D, bool HP>
-static hipError_t launch_split_t(const BwdArgs& a, hipStream_t st) {
+static hipError_t launch_split_t(const BwdArgs& a, int part, hipStream_t st) {
   constexpr int NW = kWaves, kRows = 16 * kWaves;
-  const int jtiles = (a.L + KVTile<D>::CH - 1) / KVTile<D>::CH;
-  const int grid = a.B * a.H * ((a.L + kRows - 1) / kRows) * jtiles * a.n_groups_q;
-  prof_begin(K_BWD_Q, st);
-  if (a.dpair)
-    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, true, true, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
-  else
-    hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, false, true, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
-  prof_end(K_BWD_Q, st);
-  // key side over query tiles; it reads the delta bwd_q3 wrote
-  const int gridk = a.B * a.H * ((a.L + kRows - 1) / kRows) * a.n_groups_k;
-  prof_begin(K_BWD_KV, st);
-  if (a.dmask)
-    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, true, true, NW>), dim3(gridk), dim3(64 * NW), 0, st, a);
-  else
-    hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, false, true, NW>), dim3(gridk), dim3(64 * NW), 0, st, a);
-  prof_end(K_BWD_KV, st);
+  if (part == 0) {
+    // bwd_q3 over the chunk's slices and every key tile
+    const int jtiles = (a.L + KVTile<D>::CH - 1) / KVTile<D>::CH;
+    const int grid = a.B * a.H * ((a.L + kRows - 1) / kRows) * jtiles * a.n_groups_q;
+    prof_begin(K_BWD_Q, st);
+    if (a.dpair)
+      hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, true, true, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
+    else
+      hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, false, true, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
+    prof_end(K_BWD_Q, st);
+  } else {
+    // key side over query tiles; it reads the delta bwd_q3 wrote
+    const int gridk = a.B * a.H * ((a.L + kRows - 1) / kRows) * a.n_groups_k;
+    prof_begin(K_BWD_KV, st);
+    if (a.dmask)
+      hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, true, true, NW>), dim3(gridk), dim3(64 * NW), 0, st, a);
+    else
+      hipLaunchKernelGGL((evo_bwd_kv3_kernel<T, D, HP, false, true, NW>), dim3(gridk), dim3(64 * NW), 0, st, a);
+    prof_end(K_BWD_KV, st);
+  }
   return hipGetLastError();
 }
 
 template <class T>
-static hipError_t launch_split_dt(const BwdArgs& a, int D, hipStream_t st) {
+static hipError_t launch_split_dt(const BwdArgs& a, int D, int part, hipStream_t st) {
   const bool hp = a.pair != nullptr;
   switch (D) {
-    case 8: return hp ? launch_split_t<T, 8, true>(a, st) : launch_split_t<T, 8, false>(a, st);
-    case 16: return hp ? launch_split_t<T, 16, true>(a, st) : launch_split_t<T, 16, false>(a, st);
-    case 32: return hp ? launch_split_t<T, 32, true>(a, st) : launch_split_t<T, 32, false>(a, st);
-    case 64: return hp ? launch_split_t<T, 64, true>(a, st) : launch_split_t<T, 64, false>(a, st);
+    case 8: return hp ? launch_split_t<T, 8, true>(a, part, st) : launch_split_t<T, 8, false>(a, part, st);
+    case 16: return hp ? launch_split_t<T, 16, true>(a, part, st) : launch_split_t<T, 16, false>(a, part, st);
+    case 32: return hp ? launch_split_t<T, 32, true>(a, part, st) : launch_split_t<T, 32, false>(a, part, st);
+    case 64: return hp ? launch_split_t<T, 64, true>(a, part, st) : launch_split_t<T, 64, false>(a, part, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_q_split(const BwdArgs& a, int D, bool bf16, hipStream_t stream) {
-  return bf16 ? launch_split_dt<BF16>(a, D, stream) : launch_split_dt<F16>(a, D, stream);
+hipError_t launch_bwd_q_split(const BwdArgs& a, int D, bool bf16, int part, hipStream_t stream) {
+  return bf16 ? launch_split_dt<BF16>(a, D, part, stream) : launch_split_dt<F16>(a, D, part, stream);
 }
 
 }  // namespace evo

@@ -42,15 +42,23 @@ struct BwdArgs {
   float* delta;          // [B,N,H,L]
   float* dmask_part;     // [B,N,H,L]   (when dmask requested)
   float* dmask_f32;      // [B,N,L]
-  float* dpair_part;     // [n_groups_q, B, H, L, L] (when dpair requested)
+  float* dpair_part;     // [n_groups_q, B, H, L, L] (when dpair requested), one chunk's
   float* dpair_f32;      // [B,H,L,L]
-  float* dq_part;        // [jtiles, B,N,L,H,D] fp32 partials of dQ (rows longer than one key tile), dense
+  float* dq_part;        // [jtiles, B, q_nc, L,H,D] fp32 partials of dQ of one chunk of slices
+                         // (rows longer than one key tile), dense
   // element strides of dims B, N, L shared by q, k, v, out, dout, dq, dk and
   // dv; the H heads of D elements of one (b, n, l) row are dense
   int64_t sB, sN, sL;
   int B, N, L, H;
   int Gq;          // slices per bwd_q3 workgroup
-  int n_groups_q;
+  int n_groups_q;  // bwd_q3 workgroups per (b, h, query tile) in the chunk
+  // bwd_q3 covers the chunk of slices [q_n0, q_n0 + q_nc) (all N when rows
+  // fit one key tile; longer rows go in chunks that bound the partials)
+  int q_n0, q_nc;
+  // the group slots of dpair_part hold running sums over the chunks: 0 for
+  // the first chunk (bwd_q3 starts from zero), 1 after it (bwd_q3 starts from
+  // the slot's sum the previous chunk left)
+  int dpair_carry;
   int Gk;          // slices per bwd_kv3 workgroup
   int n_groups_k;
   float scale;
@@ -74,8 +82,8 @@ hipError_t launch_fwd(FwdArgs a, int D, bool bf16, hipStream_t stream);
 hipError_t launch_bwd(BwdArgs a, int D, bool bf16, hipStream_t stream);
 // backward for rows that fit one key tile (L <= 256, or 128 at D = 64): bwd_q3 then bwd_kv3
 hipError_t launch_bwd_tile(const BwdArgs& a, int D, bool bf16, hipStream_t stream);
-// longer rows: bwd_q3 with one key tile per workgroup (dQ left as fp32
-// partials), then bwd_kv3 over query tiles
-hipError_t launch_bwd_q_split(const BwdArgs& a, int D, bool bf16, hipStream_t stream);
+// longer rows: part 0 is bwd_q3 over one chunk of slices with one key tile
+// per workgroup (dQ left as fp32 partials), part 1 bwd_kv3 over query tiles
+hipError_t launch_bwd_q_split(const BwdArgs& a, int D, bool bf16, int part, hipStream_t stream);
 
 }  // namespace evo

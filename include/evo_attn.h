@@ -59,7 +59,7 @@ typedef enum {
   EVO_ERR_HEAD_DIM = 4,          /* D not in {8, 16, 32, 64} */
   EVO_ERR_ALIGNMENT = 5,         /* a pointer is not 16-byte aligned */
   EVO_ERR_NOT_DEVICE_MEMORY = 6, /* a pointer is not device memory of the current device */
-  EVO_ERR_WORKSPACE = 7,         /* workspace NULL or smaller than evo_attn_bwd_workspace_bytes() */
+  EVO_ERR_WORKSPACE = 7,         /* workspace NULL or smaller than evo_attn_bwd_workspace_bytes_within(..., 0) */
   EVO_ERR_DEVICE = 8,            /* the current device is not gfx950 */
   EVO_ERR_LAUNCH = 9,            /* a kernel launch failed */
   EVO_ERR_ALIAS = 10,            /* an output overlaps an input or another output */
@@ -89,8 +89,20 @@ evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const voi
                           const void* pair_bias, void* out, float* lse, const int64_t shape[5],
                           int dtype, void* stream);
 
-/* Bytes of device workspace evo_attn_bwd needs for this problem (0 on bad arguments). */
+/* Bytes of device workspace for evo_attn_bwd on this problem (0 on bad
+ * arguments): fp32 delta and bias-gradient accumulators, the dpair partials of
+ * the slice groups and, for rows longer than one key tile (L > 256, or > 128
+ * at D = 64), the fp32 dQ partials of each key tile.  The backward fits its
+ * plan to the workspace it is given: with less room it takes the slices of
+ * long rows in chunks (more launches, smaller partials).  This size is that
+ * of the plan with at most 384 MiB of partials; evo_attn_bwd_workspace_bytes_within
+ * gives the size for another bound on the partials (0: the least workspace
+ * the backward accepts).  The workspace size is an input of the plan: the bias
+ * gradients' summation order, hence their last bits, can depend on it, and a
+ * call is bitwise reproducible for the same arguments. */
 size_t evo_attn_bwd_workspace_bytes(const int64_t shape[5], int dtype, int has_mask, int has_pair);
+size_t evo_attn_bwd_workspace_bytes_within(const int64_t shape[5], int dtype, int has_mask, int has_pair,
+                                           size_t partial_budget);
 
 /* Byte offsets into the workspace, valid after evo_attn_bwd returns and its
  * work completes, of the fp32 accumulators the bias gradients are cast from:
@@ -110,8 +122,9 @@ evo_status_t evo_attn_bwd_workspace_offsets(const int64_t shape[5], int dtype, i
  *   dq, dk, dv  [B,N,L,H,D] dtype  outputs
  *   dmask_bias  [B,N,1,1,L] dtype  output: sum over h and i of dS; may be NULL (not computed)
  *   dpair_bias  [B,1,H,L,L] dtype  output: sum over n of dS;       may be NULL (not computed)
- *   workspace, workspace_bytes     device scratch of at least evo_attn_bwd_workspace_bytes(),
- *                                  contents undefined on entry; see evo_attn_bwd_workspace_offsets
+ *   workspace, workspace_bytes     device scratch of at least evo_attn_bwd_workspace_bytes_within(..., 0)
+ *                                  (evo_attn_bwd_workspace_bytes() for the default plan), contents
+ *                                  undefined on entry; see evo_attn_bwd_workspace_offsets
  * The bias gradients are accumulated in fp32 in a fixed order (the result
  * is bitwise reproducible) and rounded to dtype to nearest even.
  * Passing dmask_bias without mask_bias, or dpair_bias without pair_bias, is
@@ -151,8 +164,9 @@ evo_status_t evo_attn_bwd_strided(const void* q, const void* k, const void* v, c
  * Arguments and results are those of evo_attn_bwd_strided (strides NULL: the
  * dense layout) without the workspace: the call allocates nothing and uses
  * instead a static device array of EVO_NOALLOC_SCRATCH_BYTES bytes (64 MiB)
- * that every GPU the library runs on holds until the process ends.  A problem
- * whose evo_attn_bwd_workspace_bytes() exceeds that limit returns
+ * that every GPU the library runs on holds until the process ends, with the
+ * plan fitted to it as to a workspace of that size.  A problem whose
+ * evo_attn_bwd_workspace_bytes_within(..., 0) exceeds that limit returns
  * EVO_ERR_SCRATCH_LIMIT before anything is enqueued.  All calls on one GPU
  * share its array, which keeps the last call's contents: calls that overlap
  * on one GPU (on different streams, or from several threads) race and must be

@@ -45,14 +45,14 @@ def max_err(a, b):
     return float(np.max(np.abs(a - b)))
 
 
-def run_gpu(cfg, bits):
+def run_gpu(cfg, bits, partial_budget=None):
     from evoformer_biased_attention_amd.attention import attn_bwd, attn_fwd, workspace_f32_views
 
     dt = cfg.dtype
     q, k, v = (to_device(bits[n], dt) for n in ("q", "k", "v"))
     m, p, do = to_device(bits["mask_bias"], dt), to_device(bits["pair_bias"], dt), to_device(bits["dout"], dt)
     out, lse = attn_fwd(q, k, v, m, p)
-    g = attn_bwd(q, k, v, m, p, out, lse, do)
+    g = attn_bwd(q, k, v, m, p, out, lse, do, partial_budget=partial_budget)
     torch.cuda.synchronize()
     delta, dmask32, dpair32 = workspace_f32_views(g["workspace"], cfg.shape, q.dtype, m is not None, p is not None)
     return {

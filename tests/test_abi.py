@@ -115,12 +115,58 @@ def test_no_usable_device_is_reported_as_evo_err_device():
 
 def test_noalloc_backward_refuses_problems_past_its_static_scratch():
     """evo_attn_bwd_noalloc works inside a static device array of
-    EVO_NOALLOC_SCRATCH_BYTES; a problem whose workspace is larger is refused
-    with EVO_ERR_SCRATCH_LIMIT before any device call."""
-    big = (1, 768, 768, 4, 32)
-    assert _lib.evo_attn_bwd_workspace_bytes(big, _lib.EVO_BF16, 1, 1) > _lib.EVO_NOALLOC_SCRATCH_BYTES
+    EVO_NOALLOC_SCRATCH_BYTES; a problem whose least workspace is larger is
+    refused with EVO_ERR_SCRATCH_LIMIT before any device call."""
+    big = (1, 2048, 1024, 4, 32)  # delta and the dmask partials alone pass 64 MiB
+    assert _lib.evo_attn_bwd_workspace_bytes_within(big, _lib.EVO_BF16, 1, 1, 0) > _lib.EVO_NOALLOC_SCRATCH_BYTES
     p = [16 * (i + 1) for i in range(13)]
     assert _lib.evo_attn_bwd_noalloc(*p, big, None, _lib.EVO_BF16, None) == _lib.EVO_ERR_SCRATCH_LIMIT
     # argument errors come first, as in evo_attn_bwd
     assert _lib.evo_attn_bwd_noalloc(*([None] * 13), (1, 2, 32, 2, 7), None, 0, None) == _lib.EVO_ERR_HEAD_DIM
     assert "EVO_NOALLOC_SCRATCH_BYTES" in _lib.evo_status_string(_lib.EVO_ERR_SCRATCH_LIMIT)
+
+
+MiB = 1 << 20
+
+
+@pytest.mark.parametrize("shape,has_pair", [((1, 768, 768, 4, 32), 1), ((1, 384, 512, 8, 32), 0),
+                                            ((2, 48, 640, 2, 64), 1), ((1, 256, 256, 4, 32), 1)])
+def test_backward_plan_fits_the_workspace(shape, has_pair):
+    """The backward fits its plan to the workspace: more room for the fp32
+    partials never gives a smaller workspace, the partials stay within the
+    budget whenever some plan fits it, the default is the plan for 384 MiB of
+    partials, and rows of one key tile do not depend on the budget at all."""
+    dt = _lib.EVO_BF16
+    within = lambda b: _lib.evo_attn_bwd_workspace_bytes_within(shape, dt, 1, has_pair, b)
+    least = within(0)
+    fixed = _lib.evo_attn_bwd_workspace_offsets(shape, dt, 1, has_pair)
+    assert least > 0
+    sizes = [within(b * MiB) for b in (0, 32, 64, 128, 160, 256, 384, 640, 4096)]
+    assert sizes == sorted(sizes)
+    assert _lib.evo_attn_bwd_workspace_bytes(shape, dt, 1, has_pair) == within(384 * MiB)
+    B, N, L, H, D = shape
+    jtiles = -(-L // (128 if D == 64 else 256))
+    if jtiles == 1:
+        assert len(set(sizes)) == 1
+        return
+    # the regions that do not depend on the plan: delta, dmask partials and
+    # accumulators, the dpair accumulator
+    fixed_bytes = sum(-(-n // 256) * 256 for n in (B * N * H * L * 4, B * N * H * L * 4, B * N * L * 4,
+                                                     (B * H * L * L * 4) if has_pair else 0))
+    slot = B * H * L * L * 4 if has_pair else 0
+    for b in (64, 128, 160, 256, 384, 640):
+        got = within(b * MiB)
+        # a plan that fits exists once one slice with one dpair slot does
+        if jtiles * B * L * H * D * 4 + slot + 512 <= b * MiB:
+            assert got - fixed_bytes <= b * MiB, (b, got)
+    # offsets of the fp32 accumulators do not depend on the plan
+    assert fixed[0] == 0
+
+
+def test_triangle_workspace_bounds():
+    """(1,768,768,4,32): the default plan keeps the long-row partials within
+    384 MiB (the whole workspace under 450 MB), and 160 MiB of partials brings
+    the workspace under 200 MB."""
+    shape = (1, 768, 768, 4, 32)
+    assert _lib.evo_attn_bwd_workspace_bytes(shape, _lib.EVO_BF16, 1, 1) < 450e6
+    assert _lib.evo_attn_bwd_workspace_bytes_within(shape, _lib.EVO_BF16, 1, 1, 160 * MiB) < 200e6
