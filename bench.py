@@ -356,8 +356,10 @@ def main():
     pad_mixed = padded(I.PADDED)
 
     def kernel_times(fn, n):
-        """Average launch time per kernel kind from the HIP events the library
-        records on this stream around each of its kernels."""
+        """Per kernel kind: average launch time (us) and launches over the n
+        calls, from the HIP events the library records on this stream around
+        each of its kernels (a backward over long rows in chunks launches
+        bwd_q3 and bwd_fin once per chunk)."""
         _lib.evo_attn_profile_read()
         _lib.evo_attn_profile_enable(True)
         for _ in range(n):
@@ -393,7 +395,8 @@ def main():
                 "shape": list(c.shape), "dtype": c.dtype, "pair_bias": c.pair_sigma is not None,
                 "fwd": {**f_, "tflops": round(tf_f, 2), "pct_peak": round(100 * tf_f / PEAK_MFMA_TFLOPS, 2)},
                 "bwd": {**b_, "tflops": round(tf_b, 2), "pct_peak": round(100 * tf_b / PEAK_MFMA_TFLOPS, 2)},
-                "kernel_us": {kk: round(vv[0], 2) for kk, vv in kt_.items()},
+                "kernel_us": {kk: round(vv[0] * vv[1] / 5, 2) for kk, vv in kt_.items()},  # per call
+                "kernel_launches": {kk: vv[1] // 5 for kk, vv in kt_.items()},
                 "workspace_bytes": int(cws.numel()),
             }
             del cq, ck, cv, cm, cp, cdo, co, cl, cws
@@ -435,8 +438,9 @@ def main():
     }
     fwd_b, bwd_b = algorithmic_bytes(cfg)
     bwd_kinds = [n for n in kernels if n.startswith("bwd")]
-    t_fwd_k = kernels["fwd"]["avg_us"] * 1e-6
-    t_bwd_k = sum(kernels[n]["avg_us"] for n in bwd_kinds) * 1e-6
+    per_step = lambda n: kernels[n]["avg_us"] * kernels[n]["launches"] / args.steps  # us per step
+    t_fwd_k = per_step("fwd") * 1e-6
+    t_bwd_k = sum(per_step(n) for n in bwd_kinds) * 1e-6
 
     def hbm(alg, t, kinds):
         cnt = [load_traffic(n, cfg.name, sha) for n in kinds]

@@ -387,7 +387,11 @@ void prof_begin(KernelKind k, hipStream_t s) {
   if (g_prof_recs.size() >= kProfMaxRecs) return;
   hipEvent_t e = prof_event();
   if (!e) return;
-  hipEventRecord(e, s);
+  if (hipEventRecord(e, s) != hipSuccess) {  // no record for this launch
+    (void)hipGetLastError();
+    g_prof_pool.push_back(e);
+    return;
+  }
   g_prof_open_kind = (int)k;
   g_prof_open_ev = e;
 }
@@ -398,8 +402,13 @@ void prof_end(KernelKind k, hipStream_t s) {
   if (g_prof_open_kind != (int)k || !g_prof_open_ev) return;
   hipEvent_t e = prof_event();
   if (!e) return;
-  hipEventRecord(e, s);
-  g_prof_recs.push_back(ProfRec{(int)k, g_prof_open_ev, e});
+  if (hipEventRecord(e, s) != hipSuccess) {  // drop the open record
+    (void)hipGetLastError();
+    g_prof_pool.push_back(e);
+    g_prof_pool.push_back(g_prof_open_ev);
+  } else {
+    g_prof_recs.push_back(ProfRec{(int)k, g_prof_open_ev, e});
+  }
   g_prof_open_kind = -1;
   g_prof_open_ev = nullptr;
 }

@@ -699,11 +699,13 @@ template <class T, int D, bool HM, bool HP>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int grid = a.B * a.H * a.i_tiles * a.n_groups;
   prof_begin(K_FWD, stream);
-  if (HP && a.L <= KVTile<D>::CH) {
-    hipLaunchKernelGGL((evo_fwd_kernel<T, D, HM, HP, KVTile<D>::CH / 32>), dim3(grid), dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((evo_fwd_kernel<T, D, HM, HP, 0>), dim3(grid), dim3(256), 0, stream, a);
+  bool resident = false;  // the pair bias held for the whole row (rows of one key tile)
+  if constexpr (HP) resident = a.L <= KVTile<D>::CH;
+  if constexpr (HP) {
+    if (resident)
+      hipLaunchKernelGGL((evo_fwd_kernel<T, D, HM, true, KVTile<D>::CH / 32>), dim3(grid), dim3(256), 0, stream, a);
   }
+  if (!resident) hipLaunchKernelGGL((evo_fwd_kernel<T, D, HM, HP, 0>), dim3(grid), dim3(256), 0, stream, a);
   prof_end(K_FWD, stream);
   return hipGetLastError();
 }
