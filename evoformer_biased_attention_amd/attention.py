@@ -86,6 +86,14 @@ def _dense_strides(shape) -> Tuple[int, int, int]:
     return (N * L * H * D, L * H * D, H * D)
 
 
+def _empty_problem(q: torch.Tensor) -> bool:
+    """A problem with no score at all (B, N, L or H zero, a supported D): there
+    is nothing to compute, and the library, whose shapes are at least 1, is
+    not called."""
+    B, N, L, H, D = q.shape
+    return q.numel() == 0 and D in (8, 16, 32, 64)
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_bias: Optional[torch.Tensor] = None,
              pair_bias: Optional[torch.Tensor] = None, need_lse: bool = True
              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
@@ -95,6 +103,10 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask_bias: Optio
     allocated nor written and None is returned in its place; out is identical.
     """
     _check_inputs(q, k, v, mask_bias, pair_bias)
+    if _empty_problem(q):
+        B, N, L, H, D = q.shape
+        out = torch.empty_like(q)
+        return out, (torch.empty((B, N, H, L), dtype=torch.float32, device=q.device) if need_lse else None)
     lay = _layout((q, k, v))
     if lay is None:
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
@@ -119,8 +131,16 @@ def attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask: bool = T
     The library fits its plan to the workspace: a given `workspace` is used as
     it is (it must hold at least the least workspace the backward accepts);
     otherwise one is allocated, of the default size or of the size for
-    `partial_budget` bytes of fp32 partials (long rows then go in chunks)."""
+    `partial_budget` bytes of fp32 partials (long rows then go in chunks).
+    A problem with no score returns empty gradients, and bias gradients that
+    sum over an empty dimension (dpair with N = 0, dmask with H = 0) are zero."""
     _check_inputs(q, k, v, mask_bias, pair_bias)
+    if _empty_problem(q):
+        return {"dq": torch.empty_like(q), "dk": torch.empty_like(q), "dv": torch.empty_like(q),
+                "dmask": torch.zeros_like(mask_bias) if (mask_bias is not None and want_dmask) else None,
+                "dpair": torch.zeros_like(pair_bias) if (pair_bias is not None and want_dpair) else None,
+                "workspace": workspace if workspace is not None else torch.empty(0, dtype=torch.uint8,
+                                                                                  device=q.device)}
     lay = _layout((q, k, v, out))
     if lay is None:
         q, k, v, out = (t.contiguous() for t in (q, k, v, out))

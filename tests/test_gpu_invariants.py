@@ -13,7 +13,10 @@ error behaviour on a real device.
 * streams: a run on a side stream gives the same bits as on the current stream;
 * argument errors (host pointer, misaligned pointer, short workspace, a bias
   gradient without its bias, an output aliasing an input) return their status
-  and leave every output untouched.
+  and leave every output untouched;
+* empty problems (B, N, L or H zero) through the Python layer: outputs of the
+  right empty shapes, and the bias gradient that sums over an empty dimension
+  (dpair with N = 0, dmask with H = 0) is exactly zero.
 """
 import numpy as np
 import pytest
@@ -167,6 +170,34 @@ def test_autograd_wrapper_equals_direct_calls():
     out_m = evoformer_attention(x["q"], x["k"], x["v"], [x["mask_bias"]])
     o3, _ = attn_fwd(x["q"], x["k"], x["v"], x["mask_bias"], None)
     assert torch.equal(out_m, o3)
+
+
+@pytest.mark.parametrize("shape", [(0, 3, 16, 2, 32), (2, 0, 16, 2, 32), (1, 3, 0, 2, 16), (1, 3, 16, 0, 8)],
+                         ids=["B0", "N0", "L0", "H0"])
+def test_empty_problems(shape):
+    from evoformer_biased_attention_amd.attention import evoformer_attention
+
+    print(f"case empty {shape}", flush=True)
+    B, N, L, H, D = shape
+    g = torch.Generator(device="cpu").manual_seed(5)
+    mk = lambda *s_: torch.randn(*s_, generator=g).to("cuda", torch.float16).requires_grad_(True)
+    q, k, v = mk(B, N, L, H, D), mk(B, N, L, H, D), mk(B, N, L, H, D)
+    m, p = mk(B, N, 1, 1, L), mk(B, 1, H, L, L)
+    out = evoformer_attention(q, k, v, [m, p])
+    assert out.shape == q.shape and out.numel() == 0
+    out.backward(torch.zeros_like(out))
+    torch.cuda.synchronize()
+    for t in (q, k, v):
+        assert t.grad.shape == t.shape
+    assert m.grad.shape == m.shape and p.grad.shape == p.shape
+    # sums over an empty dimension are zero
+    assert bool((m.grad == 0).all()) and bool((p.grad == 0).all())
+    if N == 0 and B * H * L > 0:
+        assert p.grad.numel() > 0
+    if H == 0 and B * N * L > 0:
+        assert m.grad.numel() > 0
+    with torch.no_grad():
+        assert evoformer_attention(q, k, v, [m, p]).shape == q.shape
 
 
 def test_offset_views_are_taken():
