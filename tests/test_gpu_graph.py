@@ -14,16 +14,24 @@ from tests.helpers import to_device
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["tiny_row", "msa_row"])
-def test_graph_replay_matches_eager(name):
+CASES = [
+    (I.CONFIGS["tiny_row"], None),
+    (I.CONFIGS["msa_row"], None),
+    # rows longer than one key tile, planned in chunks (a 24 MiB partial
+    # budget): bwd_q3 and bwd_fin launched once per chunk
+    (I.custom("graph_chunked_l640_d64_bf16", 2, 24, 640, 2, 64, "bf16", 0.05, 1.0, 51), 24 << 20),
+]
+
+
+@pytest.mark.parametrize("cfg,budget", CASES, ids=[c.name for c, _ in CASES])
+def test_graph_replay_matches_eager(cfg, budget):
     from evoformer_biased_attention_amd.attention import attn_bwd, attn_fwd
 
-    cfg = I.CONFIGS[name]
-    print(f"case graph replay {name} shape={cfg.shape}", flush=True)
+    print(f"case graph replay {cfg.name} shape={cfg.shape} partial budget={budget}", flush=True)
     bits = I.make_inputs(cfg)
     q, k, v, m, p, do = (to_device(bits[n], cfg.dtype) for n in ("q", "k", "v", "mask_bias", "pair_bias", "dout"))
     out_e, lse_e = attn_fwd(q, k, v, m, p)
-    g_e = attn_bwd(q, k, v, m, p, out_e, lse_e, do)
+    g_e = attn_bwd(q, k, v, m, p, out_e, lse_e, do, partial_budget=budget)
     torch.cuda.synchronize()
     ref = [t.clone() for t in (out_e, lse_e, g_e["dq"], g_e["dk"], g_e["dv"], g_e["dmask"], g_e["dpair"])]
 
@@ -36,7 +44,7 @@ def test_graph_replay_matches_eager(name):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         out_g, lse_g = attn_fwd(q, k, v, m, p)
-        g_g = attn_bwd(q, k, v, m, p, out_g, lse_g, do)
+        g_g = attn_bwd(q, k, v, m, p, out_g, lse_g, do, partial_budget=budget)
     got = (out_g, lse_g, g_g["dq"], g_g["dk"], g_g["dv"], g_g["dmask"], g_g["dpair"])
     for rep in range(4):
         graph.replay()
