@@ -36,7 +36,8 @@ namespace evo {
 
 constexpr int kFwdWaves = 4;
 constexpr int kFwdRows = 32 * kFwdWaves;  // query rows per workgroup
-constexpr float kTauNat = 5.545177444479562f;  // 8 * ln 2
+constexpr float kTau2 = 8.f;  // the exponent base may lag the row max by up to 8 (log2 units)
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kFastSum = 256.f;  // 2^8: a block sum below it keeps the exponent base (no block max)
 
 // Key tiles of the forward without a pair bias at D <= 32: 128 keys (256 at
@@ -67,33 +68,60 @@ struct FwdShape {
   static constexpr int MB = (D + 31) / 32;        // 32-row blocks of O^T
 };
 
-// Pair-bias values for one 32-key block in the S^T accumulator layout:
-// lane (query i) gets pair[i][j0 + 8q + 4*(l/32) + u], q,u = 0..3, packed two per dword.
-// Branch-free: rows and columns are clamped into range and the values of
-// columns >= L are replaced by zero (those keys are masked to -inf later).
-__device__ __forceinline__ void load_pair_block(u32x2 (&dst)[4], const uint16_t* prow, int j0, int L, int half,
-                                                bool vec_ok) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int j = j0 + 8 * q + 4 * half;
-    u32x2 v;
-    if (vec_ok) {  // uniform: L % 4 == 0, so j + 3 < L whenever j < L
-      v = *reinterpret_cast<const u32x2*>(prow + min(j, L - 4));
-      if (j >= L) v = u32x2{0u, 0u};
-    } else {
-      uint32_t t[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) t[u] = (j + u < L) ? (uint32_t)prow[min(j + u, L - 1)] : 0u;
-      v[0] = t[0] | (t[1] << 16);
-      v[1] = t[2] | (t[3] << 16);
-    }
-    dst[q] = v;
-  }
+// bf16 pair-bias bits for the bias product: -inf (and the NaNs of negative
+// sign) become the most negative finite value, whose product with the
+// diagonal's sqrt(D) still overflows to -inf in fp32 while the zeros off the
+// diagonal give 0, not 0 * inf = NaN.  One packed 16-bit minimum per two values.
+__device__ __forceinline__ uint32_t bf16x2_no_neg_inf(uint32_t w) {
+  using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
+  const u16x2 lim = {(unsigned short)0xFF7F, (unsigned short)0xFF7F};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, w), lim));
 }
 
-__device__ __forceinline__ uint16_t pick16(const u32x2 (&b)[4], int r) {
-  uint32_t w = b[r / 4][(r % 4) / 2];
-  return (r & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
+// Pair-bias values of one 32-key block, 16 per lane (query i, half), in one of
+// two orders.  kMfma: the B operand of the bias product, which adds the bias
+// to the S^T accumulator through the MFMA (an identity over the block's keys,
+// scaled by sqrt(D) as the mask term is, times the pair rows): position
+// 8 s + e holds pair[i][j0 + 16 s + 8 half + e].  Otherwise the S^T accumulator
+// order, for a bias added to the scores by the VALU: position 4 q + u holds
+// pair[i][j0 + 8 q + 4 half + u].  Columns >= L read zero (those keys are
+// masked to -inf by the mask term).  vec: L is a multiple of the run of
+// consecutive keys (8 or 4), so the runs are aligned vector loads.  The MFMA
+// order is that of bf16 and takes its -inf values out (bf16x2_no_neg_inf).
+template <bool kMfma>
+__device__ __forceinline__ void load_pair_ops(short8_t (&dst)[2], const uint16_t* prow, int j0, int L, int half,
+                                              bool vec) {
+  constexpr int G = kMfma ? 8 : 4;  // consecutive keys per run
+  uint32_t w[8];
+#pragma unroll
+  for (int g = 0; g < 16 / G; ++g) {
+    const int j = j0 + (kMfma ? 16 * g + 8 * half : 8 * g + 4 * half);
+    if (vec) {  // uniform; j + G - 1 < L whenever j < L
+      if constexpr (kMfma) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(prow + min(j, L - G));
+        if (j >= L) v = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[4 * g + e] = v[e];
+      } else {
+        u32x2 v = *reinterpret_cast<const u32x2*>(prow + min(j, L - G));
+        if (j >= L) v = u32x2{0u, 0u};
+        w[2 * g] = v[0];
+        w[2 * g + 1] = v[1];
+      }
+    } else {
+      uint32_t t[G];
+#pragma unroll
+      for (int e = 0; e < G; ++e) t[e] = (j + e < L) ? (uint32_t)prow[min(j + e, L - 1)] : 0u;
+#pragma unroll
+      for (int e = 0; e < G; e += 2) w[(g * G + e) / 2] = t[e] | (t[e + 1] << 16);
+    }
+  }
+  if constexpr (kMfma) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = bf16x2_no_neg_inf(w[e]);
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) dst[s] = __builtin_bit_cast(short8_t, u32x4{w[4 * s], w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]});
 }
 
 template <class T, int D, bool HAS_MASK, bool HAS_PAIR, int RES>
@@ -101,10 +129,6 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
   using S = FwdShape<D>;
   using TL = FwdTile<D, HAS_PAIR>;
   constexpr int kMcBufs = (std::is_same<T, F16>::value && D <= 32) ? 2 : 1;
-  // the block max only when needed (A/B on one MI355X: (1,384,512,8,32) bf16
-  // forward -1.6%, the other shapes within the noise); not for bf16 with a
-  // resident pair bias, where its extra registers spill (+5% at (1,512,256,8,8))
-  constexpr bool kSkipMax = !(std::is_same<T, BF16>::value && RES > 0);
   // two K/V tile buffers; with a resident pair bias the same bytes first hold
   // the workgroup's 128 x (32 RES) bias slab
   constexpr int kSlab = RES > 0 ? kFwdRows * RES * 64 : 0;
@@ -141,10 +165,14 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
   const int nchunks = (L + TL::CH - 1) / TL::CH;
   const int ntiles = (n_end - n_begin) * nchunks;
 
-  // ---- pair-bias registers (loaded once when the whole row fits one tile)
-  u32x2 pres[RES > 0 ? RES : 1][4];
+  // ---- pair-bias values (held for the whole kernel when the row fits one tile).
+  // bf16 adds them through the MFMA (no mixed-precision FMA takes a bf16
+  // operand, so the VALU would first widen each value); fp16 adds them in the
+  // VALU (one mixed-precision FMA per score costs less than the extra MFMAs).
+  constexpr bool kPairMfma = HAS_PAIR && std::is_same<T, BF16>::value;
+  short8_t pres[RES > 0 ? RES : 1][2];
   const uint16_t* prow = nullptr;
-  const bool pvec = (L % 4) == 0;
+  const bool pvec = (L % (kPairMfma ? 8 : 4)) == 0;
   if constexpr (HAS_PAIR) {
     prow = a.pair + (((size_t)b * H + h) * L + ic) * L;
     if constexpr (RES > 0) {
@@ -174,17 +202,53 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
 #pragma unroll
         for (int kb = 0; kb < RES; ++kb)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c = 4 * kb + q;  // chunk holding keys 32 kb + 8 q .. +7
-            pres[kb][q] = *reinterpret_cast<const u32x2*>(smem + (r * RC + ((c ^ (r & 15)) % RC)) * 16 + 8 * half);
+          for (int s2 = 0; s2 < 2; ++s2) {
+            if constexpr (kPairMfma) {
+              const int c = 4 * kb + 2 * s2 + half;  // chunk holding keys 32 kb + 16 s2 + 8 half .. +7
+              u32x4 v = *reinterpret_cast<const u32x4*>(smem + (r * RC + ((c ^ (r & 15)) % RC)) * 16);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = bf16x2_no_neg_inf(v[e]);
+              pres[kb][s2] = __builtin_bit_cast(short8_t, v);
+            } else {
+              // keys 32 kb + 8 q + 4 half .. +3 for q = 2 s2, 2 s2 + 1: the
+              // half-chunk at byte 8 half of chunk 4 kb + q
+              const int c0 = 4 * kb + 2 * s2, c1 = c0 + 1;
+              const u32x2 v0 = *reinterpret_cast<const u32x2*>(smem + (r * RC + ((c0 ^ (r & 15)) % RC)) * 16 + 8 * half);
+              const u32x2 v1 = *reinterpret_cast<const u32x2*>(smem + (r * RC + ((c1 ^ (r & 15)) % RC)) * 16 + 8 * half);
+              pres[kb][s2] = __builtin_bit_cast(short8_t, u32x4{v0[0], v0[1], v1[0], v1[1]});
+            }
           }
         __syncthreads();  // the slab area is reused by the K/V tiles
       } else {
 #pragma unroll
-        for (int kb = 0; kb < RES; ++kb) load_pair_block(pres[kb], prow, kb * 32, L, half, pvec);
+        for (int kb = 0; kb < RES; ++kb) load_pair_ops<kPairMfma>(pres[kb], prow, kb * 32, L, half, pvec);
       }
     }
   }
+
+  // A operands of the bias product: sqrt(D) on the diagonal of the block's
+  // keys, so the product adds sqrt(D) pair[i][j] to S^T[j][i] as the mask term
+  // adds sqrt(D) mask[j]; for k-step s, lane (key m, half) holds it at position
+  // m - 16 s - 8 half when that lies in 0..7.  sqrt(D) is exact in 16 bits at
+  // D = 16 and 64; at D = 8 and 32 it is taken as the dtype's rounding plus the
+  // rounding of the remainder, a second product (one 16-bit value alone is off
+  // by 1.1e-4 relative; the two together by under 3e-7).  The products are
+  // exact in fp32, the sums are the accumulator's.
+  constexpr int kSqParts = (D == 16 || D == 64) ? 1 : 2;
+  short8_t pid[kPairMfma ? kSqParts : 1][2];
+  if constexpr (kPairMfma) {
+    const uint16_t hi = T::from_f32(a.sqrt_d);
+    const uint16_t lo = T::from_f32(a.sqrt_d - T::to_f32(hi));
+    const int m = lane & 31;
+#pragma unroll
+    for (int u = 0; u < kSqParts; ++u)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pid[u][s2][e] = (m == 16 * s2 + 8 * half + e) ? (short)(u ? lo : hi) : (short)0;
+  }
+  // scale to log2 units of an accumulator that holds every term of the score
+  const float c1 = a.scale * kLog2e;
 
   short8_t qop[S::KSTEPS_D], qnext[S::KSTEPS_D];
   uint32_t mraw = 0;  // this thread's mask value for the next tile (thread < CH)
@@ -282,7 +346,8 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
   };
 
   floatx16 oacc[S::MB];
-  float m_used = kNegInf, l_part = 0.f, l_part2 = 0.f;  // row sum in two chains
+  // m_used: the row's exponent base in log2 units; the row sum in two chains
+  float m_used = kNegInf, l_part = 0.f, l_part2 = 0.f;
 
   // Per-lane byte offsets within a tile buffer.  The swizzle repeats every 16
   // rows, so block jb of a tile adds the constant 32 jb rows, which goes into
@@ -348,16 +413,24 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
       });
     }
   };
-  // ---- S^T block = K Q^T + sqrt(D) mask for 32 keys
-  auto qk_block = [&](const short8_t (&kop_in)[S::KSTEPS_D], const floatx16& minit) -> floatx16 {
+  // ---- S^T block = K Q^T + sqrt(D) mask + sqrt(D) pair for 32 keys
+  auto qk_block = [&](const short8_t (&kop_in)[S::KSTEPS_D], const floatx16& minit,
+                      const short8_t (&pq)[2]) -> floatx16 {
     floatx16 acc = HAS_MASK ? minit : floatx16{};
 #pragma unroll
     for (int s = 0; s < S::KSTEPS_D; ++s) acc = T::mfma(kop_in[s], qop[s], acc);
+    if constexpr (kPairMfma) {
+#pragma unroll
+      for (int u = 0; u < kSqParts; ++u) {
+        acc = T::mfma(pid[u][0], pq[0], acc);
+        acc = T::mfma(pid[u][1], pq[1], acc);
+      }
+    }
     return acc;
   };
 
   // ---- bias, online softmax and O^T += V^T P^T for one block whose scores are in acc
-  auto softmax_pv = [&](const floatx16& acc, const int tb, auto jbc, const u32x2 (&pb)[4],
+  auto softmax_pv = [&](const floatx16& acc, const int tb, auto jbc, const short8_t (&pb)[2],
                         short8_t (&kpre)[S::KSTEPS_D], floatx16& mpre, auto prec, const bool pre_live) {
     constexpr int jb = decltype(jbc)::value, jb_pre = decltype(prec)::value;
     const uint32_t bufa = lds_addr(smem + tb * TL::BUF_BYTES);
@@ -383,126 +456,92 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
         vt[(t * S::MB + mb2) * 2 + 1] = lds_tr_imm<off>(bufa + voff[mb2][1]);
       });
     });
-    float sv[16];
-    if constexpr (HAS_PAIR) {
+    // the scores in log2 units are sc * cf
+    float sc[16];
+    float cf = c1;
+    if constexpr (HAS_PAIR && !kPairMfma) {
 #pragma unroll
       for (int rr = 0; rr < 16; rr += 2) {
-        const uint32_t w = pb[rr / 4][(rr % 4) / 2];
-        sv[rr] = T::fma_mix_lo(acc[rr], a.scale, w);
-        sv[rr + 1] = T::fma_mix_hi(acc[rr + 1], a.scale, w);
+        const uint32_t w = __builtin_bit_cast(u32x4, pb[rr / 8])[(rr % 8) / 2];
+        sc[rr] = T::fma_mix_lo(acc[rr], a.scale, w);
+        sc[rr + 1] = T::fma_mix_hi(acc[rr + 1], a.scale, w);
       }
+      cf = kLog2e;
     } else {
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sv[rr] = acc[rr] * a.scale;
+      for (int rr = 0; rr < 16; ++rr) sc[rr] = acc[rr];
     }
-    // The exponent base moves only when it has to (the base may lag the row
-    // max by up to 8 in log2 units; exp values stay below 2^8 that way).
     uint32_t pk[8];
-    if constexpr (kSkipMax) {
-      // The exps are first taken against the current base m_used: if a row's
-      // block sum stays below 2^8 in both halves, each of its probabilities
-      // does, so no score lies more than 8 (log2 units) above the base and the
-      // max-first rule would keep the base too: the row's block is done
-      // without its maximum.  Otherwise (or on the first block of a row, whose
-      // base is still -inf) the block max is formed and the row's base moved to
-      // it when it exceeds the old one by more than 8 (log2 units), rescaling
-      // the O^T accumulator and the row sums, and the exps are taken again.
-      // Both rules give the same base and the same sums (up to the rounding of
-      // the comparison itself), so the two kernels agree bit for bit.
-      float bs0, bs1;  // block sums, two chains
-      auto exps = [&](const float neg_ml) {
-        bs0 = 0.f;
-        bs1 = 0.f;
+    // The exponent base moves only when it has to: it may lag the row max by up
+    // to 8 (log2 units), so exp values stay below 2^8.
+    // The exps are first taken against the current base m_used: if a row's
+    // block sum stays below 2^8 in both halves, each of its probabilities
+    // does, so no score lies more than 8 (log2 units) above the base and the
+    // max-first rule would keep the base too: the row's block is done
+    // without its maximum.  Otherwise (or on the first block of a row, whose
+    // base is still -inf) the block max is formed and the row's base moved to
+    // it when it exceeds the old one by more than 8 (log2 units), rescaling
+    // the O^T accumulator and the row sums, and the exps are taken again.
+    // Both rules give the same base and the same sums (up to the rounding of
+    // the comparison itself), so a row's result does not depend on the rule
+    // its block took.
+    float bs0, bs1;  // block sums, two chains
+    auto exps = [&](const float neg_ml) {
+      bs0 = 0.f;
+      bs1 = 0.f;
 #pragma unroll
-        for (int rr = 0; rr < 16; rr += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr], kLog2e, neg_ml));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr + 1], kLog2e, neg_ml));
-          pk[rr / 2] = T::pack2(p0, p1);
-          // fp16: the rounded pair by v_dot2; bf16 sums the fp32 values
-          if ((rr / 2) & 1) {
-            bs1 = T::rowsum_add(bs1, p0, p1, pk[rr / 2]);
-          } else {
-            bs0 = T::rowsum_add(bs0, p0, p1, pk[rr / 2]);
-          }
+      for (int rr = 0; rr < 16; rr += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rr], cf, neg_ml));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rr + 1], cf, neg_ml));
+        pk[rr / 2] = T::pack2(p0, p1);
+        // fp16: the rounded pair by v_dot2; bf16 sums the fp32 values
+        if ((rr / 2) & 1) {
+          bs1 = T::rowsum_add(bs1, p0, p1, pk[rr / 2]);
+        } else {
+          bs0 = T::rowsum_add(bs0, p0, p1, pk[rr / 2]);
         }
-      };
-      // The choice is made per query row (the lane and its partner half), so a
-      // row's bits never depend on the other rows of the wave.
-      const bool first = m_used == kNegInf;
-      bool redo = first;
-      if (__builtin_amdgcn_ballot_w64(!first) != 0) {
-        exps(first ? 0.f : -m_used * kLog2e);
-        redo = first || !(bs0 + bs1 < kFastSum);
       }
-      if (__builtin_amdgcn_ballot_w64(redo) != 0) {
-        {  // the row redoes when either half of it does
-          float fa = redo ? 1.f : 0.f, fb = fa;
-          xhalf_swap(fa, fb);
-          redo = (fa + fb) > 0.f;
-        }
-        // block max in two chains of three-input maxima.  Written as assembly:
-        // the scores come out of assembly (v_fma_mix_f32), so the compiler would
-        // first canonicalize them for its own maximum; scores are never NaN for
-        // finite inputs.
-        auto max3 = [](float x, float y, float z) {
-          float r;
-          asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
-          return r;
-        };
-        float mb0 = max3(sv[0], sv[1], sv[2]), mb1 = max3(sv[8], sv[9], sv[10]);
-        mb0 = max3(mb0, sv[3], sv[4]);
-        mb1 = max3(mb1, sv[11], sv[12]);
-        mb0 = max3(mb0, sv[5], sv[6]);
-        mb1 = max3(mb1, sv[13], sv[14]);
-        mb0 = max3(mb0, mb1, sv[7]);
-        float mb = max3(mb0, sv[15], sv[15]);
-        {  // with the partner half (lane ^ 32) holding the same query row
-          float pa = mb, pb = mb;
-          xhalf_swap(pa, pb);
-          mb = max3(pa, pb, pb);
-        }
-        // rows that keep their base recompute the same exps
-        const bool need = redo && mb > m_used + kTauNat;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-          const float m_new = need ? mb : m_used;
-          const float alpha = need ? __builtin_amdgcn_exp2f((m_used - m_new) * kLog2e) : 1.f;
-          m_used = m_new;
-          l_part *= alpha;
-          l_part2 *= alpha;
-#pragma unroll
-          for (int mb2 = 0; mb2 < S::MB; ++mb2)
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) oacc[mb2][rr] *= alpha;
-        }
-        exps((m_used == kNegInf) ? 0.f : -m_used * kLog2e);
+    };
+    // The choice is made per query row (the lane and its partner half), so a
+    // row's bits never depend on the other rows of the wave.
+    const bool first = m_used == kNegInf;
+    bool redo = first;
+    if (__builtin_amdgcn_ballot_w64(!first) != 0) {
+      exps(first ? 0.f : -m_used);
+      redo = first || !(bs0 + bs1 < kFastSum);
+    }
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+      {  // the row redoes when either half of it does
+        float fa = redo ? 1.f : 0.f, fb = fa;
+        xhalf_swap(fa, fb);
+        redo = (fa + fb) > 0.f;
       }
-      l_part += bs0;
-      l_part2 += bs1;
-
-    } else {
-      // bf16 with a resident pair bias (at the register limit): the block max
-      // first, then the exps
+      // block max in two chains of three-input maxima.  Written as assembly:
+      // the scores come out of the MFMA or of assembly (v_fma_mix_f32), so
+      // the compiler would first canonicalize them for its own maximum;
+      // scores are never NaN for finite inputs.
       auto max3 = [](float x, float y, float z) {
         float r;
         asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
         return r;
       };
-      float mb0 = max3(sv[0], sv[1], sv[2]), mb1 = max3(sv[8], sv[9], sv[10]);
-      mb0 = max3(mb0, sv[3], sv[4]);
-      mb1 = max3(mb1, sv[11], sv[12]);
-      mb0 = max3(mb0, sv[5], sv[6]);
-      mb1 = max3(mb1, sv[13], sv[14]);
-      mb0 = max3(mb0, mb1, sv[7]);
-      float mb = max3(mb0, sv[15], sv[15]);
-      {
-        float pa = mb, pb = mb;
-        xhalf_swap(pa, pb);
-        mb = max3(pa, pb, pb);
+      float mb0 = max3(sc[0], sc[1], sc[2]), mb1 = max3(sc[8], sc[9], sc[10]);
+      mb0 = max3(mb0, sc[3], sc[4]);
+      mb1 = max3(mb1, sc[11], sc[12]);
+      mb0 = max3(mb0, sc[5], sc[6]);
+      mb1 = max3(mb1, sc[13], sc[14]);
+      mb0 = max3(mb0, mb1, sc[7]);
+      float mb = max3(mb0, sc[15], sc[15]);
+      {  // with the partner half (lane ^ 32) holding the same query row
+        float xa = mb, xb = mb;
+        xhalf_swap(xa, xb);
+        mb = max3(xa, xb, xb) * cf;  // cf > 0: the max in log2 units
       }
-      const bool need = mb > m_used + kTauNat;
+      // rows that keep their base recompute the same exps
+      const bool need = redo && mb > m_used + kTau2;
       if (__builtin_amdgcn_ballot_w64(need)) {
         const float m_new = need ? mb : m_used;
-        const float alpha = need ? __builtin_amdgcn_exp2f((m_used - m_new) * kLog2e) : 1.f;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_used - m_new) : 1.f;
         m_used = m_new;
         l_part *= alpha;
         l_part2 *= alpha;
@@ -511,22 +550,10 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) oacc[mb2][rr] *= alpha;
       }
-      const float neg_ml = (m_used == kNegInf) ? 0.f : -m_used * kLog2e;
-      float bs0 = 0.f, bs1 = 0.f;  // summed as the other branch sums
-#pragma unroll
-      for (int rr = 0; rr < 16; rr += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr], kLog2e, neg_ml));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr + 1], kLog2e, neg_ml));
-        pk[rr / 2] = T::pack2(p0, p1);
-        if ((rr / 2) & 1) {
-          bs1 = T::rowsum_add(bs1, p0, p1, pk[rr / 2]);
-        } else {
-          bs0 = T::rowsum_add(bs0, p0, p1, pk[rr / 2]);
-        }
-      }
-      l_part += bs0;
-      l_part2 += bs1;
+      exps((m_used == kNegInf) ? 0.f : -m_used);
     }
+    l_part += bs0;
+    l_part2 += bs1;
     // the V^T and prefetch reads complete here, after the exps (the packed
     // probabilities are operands of the wait)
     u32x4 bop[2] = {u32x4{pk[0], pk[1], pk[2], pk[3]}, u32x4{pk[4], pk[5], pk[6], pk[7]}};
@@ -572,10 +599,10 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
     }
     // streamed pair bias: this tile's blocks are loaded before the next tile's
     // copies are issued, so waiting for them never waits for the prefetch
-    u32x2 ptile[RES > 0 || !HAS_PAIR ? 1 : TL::CH / 32][4];
+    short8_t ptile[RES > 0 || !HAS_PAIR ? 1 : TL::CH / 32][2];
     if constexpr (RES == 0 && HAS_PAIR) {
 #pragma unroll
-      for (int jb = 0; jb < TL::CH / 32; ++jb) load_pair_block(ptile[jb], prow, kc0 + jb * 32, L, half, pvec);
+      for (int jb = 0; jb < TL::CH / 32; ++jb) load_pair_ops<kPairMfma>(ptile[jb], prow, kc0 + jb * 32, L, half, pvec);
     }
     if (t + 1 < ntiles) {
       issue_tile(t + 1);
@@ -620,23 +647,29 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
         lds_wait_all(none, kreg[0]);
         lds_wait_all(none, kreg[1]);
       }
-      sacc[0] = qk_block(kreg[0], mcb[0]);
+      // pair-bias values of block j (a dummy without a pair bias)
+      auto pops = [&](auto jc) -> const short8_t(&)[2] {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (RES > 0) {
+          return pres[j < RES ? j : 0];
+        } else {
+          return ptile[HAS_PAIR ? j : 0];
+        }
+      };
+      sacc[0] = qk_block(kreg[0], mcb[0], pops(std::integral_constant<int, 0>{}));
       static_for<0, NB>([&](auto jbc) {
         constexpr int jb = decltype(jbc)::value;
         if (jb < nblk) {
           if constexpr (jb + 1 < NB) {
-            if (jb + 1 < nblk) sacc[(jb + 1) & 1] = qk_block(kreg[(jb + 1) & 1], mcb[msel(jb + 1)]);
+            if (jb + 1 < nblk)
+              sacc[(jb + 1) & 1] = qk_block(kreg[(jb + 1) & 1], mcb[msel(jb + 1)],
+                                            pops(std::integral_constant<int, jb + 1>{}));
           }
           // the K operands of block jb + 2 are read only when it exists
           const bool pre_live = jb + 2 < nblk;
           constexpr int jpre = jb + 2 < NB ? jb + 2 : -1;
-          if constexpr (RES > 0) {
-            softmax_pv(sacc[jb & 1], tb, jbc, pres[jb < RES ? jb : 0], kreg[jb & 1], mcb[msel(jb + 2)],
-                       std::integral_constant<int, jpre>{}, pre_live);
-          } else {
-            softmax_pv(sacc[jb & 1], tb, jbc, ptile[HAS_PAIR ? jb : 0], kreg[jb & 1], mcb[msel(jb + 2)],
-                       std::integral_constant<int, jpre>{}, pre_live);
-          }
+          softmax_pv(sacc[jb & 1], tb, jbc, pops(jbc), kreg[jb & 1], mcb[msel(jb + 2)],
+                     std::integral_constant<int, jpre>{}, pre_live);
         }
       });
     }
@@ -685,7 +718,7 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
             if (i_valid && d < D) *reinterpret_cast<u32x4*>(orow + d) = w;
           }
         if (i_valid && half == 0 && a.lse != nullptr) {
-          const float lse = (m_used == kNegInf || !(l_tot > 0.f)) ? kNegInf : m_used + __logf(l_tot);
+          const float lse = (m_used == kNegInf || !(l_tot > 0.f)) ? kNegInf : __builtin_fmaf(m_used, kLn2, __logf(l_tot));
           a.lse[(((size_t)b * N + n) * H + h) * L + i] = lse;
         }
       }

@@ -81,7 +81,8 @@ typedef enum {
  * -inf, so a padded batch masked with -inf costs less than its full length (the
  * block-sparse principle of the page "DeepSpeed Sparse Attention 深度解析", section
  * 核心思想: only the blocks a mask leaves are computed; applied here to padding).  A
- * finite mask, however large, is computed.  With lse NULL the
+ * finite mask, however large, is computed.  A pair_bias entry of -inf makes that score
+ * -inf (P = 0 there), as the mask does for a whole key.  With lse NULL the
  * call is a forward for inference (the guide's §3.2 notes the forward kernels pay off
  * at inference for every attention type): out is the same, bit for bit, and nothing is
  * kept for a backward. */

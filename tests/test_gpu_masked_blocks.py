@@ -9,8 +9,9 @@ paths run: padded batches (fp16, where -1e9 overflows to -inf, and bf16 with an
 explicit -inf), whole key tiles past a row's padding, interior blocks of -inf
 keys (computed, and exact either way), a whole slice with every key masked
 (O = 0, lse = -inf, zero gradients), rows of one and of several key tiles,
-D = 8, 16, 32 and 64, with and without the pair bias.  Tolerances and the
-comparison are those of the other parity tests.
+D = 8, 16, 32 and 64, with and without the pair bias, and -inf entries in the
+pair bias itself.  Tolerances and the comparison are those of the other parity
+tests.
 """
 import numpy as np
 import pytest
@@ -125,3 +126,42 @@ def test_parity_benchmark_padded_workloads(cfg):
     bits = I.make_inputs(cfg)
     res = _run_gpu(cfg, bits)
     _compare(cfg, bits, res)
+
+
+PAIR_INF = [
+    I.custom("pinf_l72_d32_bf16_slab", 1, 3, 72, 2, 32, "bf16", 0.05, 1.0, 71),
+    I.custom("pinf_l77_d16_bf16", 1, 2, 77, 2, 16, "bf16", 0.05, 1.0, 72),
+    I.custom("pinf_l300_d32_bf16_streamed", 1, 2, 300, 2, 32, "bf16", 0.05, 1.0, 73),
+    I.custom("pinf_l96_d64_bf16", 1, 2, 96, 2, 64, "bf16", None, 1.0, 74),
+    I.custom("pinf_l40_d8_bf16", 1, 3, 40, 2, 8, "bf16", 0.1, 1.0, 75),
+    I.custom("pinf_l100_d32_fp16", 1, 3, 100, 2, 32, "fp16", 0.05, 1.0, 76),
+]
+
+
+@pytest.mark.parametrize("cfg", PAIR_INF, ids=[c.name for c in PAIR_INF])
+def test_parity_pair_bias_neg_inf(cfg):
+    """-inf entries in the pair bias: 5% of them at seeded positions, one query row
+    of head 0 entirely (that row of every slice has O = 0, lse = -inf and zero
+    dQ) and one key column of head 1 entirely.  Such a score is -inf, as with the
+    mask: P = 0 there, no NaN anywhere (bf16 adds the pair bias through the MFMA,
+    whose zeros off the diagonal meet it), and the gradients are the oracle's."""
+    print(f"case pair -inf {cfg.name} shape={cfg.shape} dtype={cfg.dtype}", flush=True)
+    bits = I.make_inputs(cfg)
+    B, N, L, H, D = cfg.shape
+    ninf = I.to_bits(np.array([NEG_INF], np.float32), cfg.dtype)[0]
+    p = bits["pair_bias"].copy()
+    rng = np.random.default_rng(cfg.seed)
+    p[rng.random(p.shape) < 0.05] = ninf
+    i_dead, j_dead = min(3, L - 1), min(5, L - 1)
+    p[:, 0, 0, i_dead, :] = ninf
+    p[:, 0, 1, :, j_dead] = ninf
+    bits["pair_bias"] = p
+    res = _run_gpu(cfg, bits)
+    for key in ("out", "lse", "dq", "dk", "dv"):
+        assert not bool(res[key].isnan().any()), f"NaN in {key}"
+    _compare(cfg, bits, res)
+    assert not bool(res["out"][:, :, i_dead, 0].any()), "O of the query row with every pair entry -inf"
+    assert bool(np.isneginf(res["lse"][:, :, 0, i_dead].cpu().numpy()).all()), "lse of that row"
+    assert not bool(res["dq"][:, :, i_dead, 0].any()), "dQ of that row"
+    assert not bool(res["dk"][:, :, j_dead, 1].any()) and not bool(res["dv"][:, :, j_dead, 1].any()), \
+        "dK, dV of the key with every pair entry -inf"
