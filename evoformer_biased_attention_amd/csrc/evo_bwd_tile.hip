@@ -97,6 +97,8 @@ __device__ __forceinline__ void issue_tile(uint8_t* buf, const uint16_t* kx, con
 //   S^T  = K Q^T + sqrt(D) mask          (mask as accumulator input)
 //   dP^T = V dO^T - delta                (-delta as accumulator input)
 //   P = exp2((S*scale + pair) log2e - lse log2e),  dS^T = P dP^T
+//                                        (bf16: sqrt(D) pair enters S^T by a
+//                                        16x16x16 MFMA against sqrt(D) I)
 //   dQ^T += K^T dS^T                     (K^T by transposed LDS reads)
 //   dpair^T[block] += I dS^T[block]      (16x16x16 MFMA against an identity)
 template <class T, int D, bool HAS_PAIR, bool WANT_DPAIR, bool SPLIT, int NW>
@@ -140,7 +142,9 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   const int ntiles = n_end - n_begin;
   const float scale = a.scale, c1 = a.scale * kLog2e;
 
-  // resident pair bias: block blk, lane gets pair[ic][kc0 + 16 blk + 4 g + 0..3]
+  // resident pair bias: block blk, lane gets pair[ic][kc0 + 16 blk + 4 g + 0..3],
+  // which is also the B operand of the 16x16x16 product that adds it (bf16)
+  constexpr bool kPairMfma = HAS_PAIR && std::is_same<T, BF16>::value;
   u32x2 pbias[HAS_PAIR ? NB : 1];
   if constexpr (HAS_PAIR) {
     const uint16_t* prow = a.pair + (((size_t)b * H + h) * L + ic) * L;
@@ -158,8 +162,24 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
         v[0] = t4[0] | (t4[1] << 16);
         v[1] = t4[2] | (t4[3] << 16);
       }
+      if constexpr (kPairMfma) {
+        v[0] = bf16x2_no_neg_inf(v[0]);
+        v[1] = bf16x2_no_neg_inf(v[1]);
+      }
       pbias[blk] = v;
     }
+  }
+  // A operands of the bias product: the parts of sqrt(D) on the diagonal,
+  // lane (key row col, group g) holding A[col][4 g + e]
+  constexpr int kSqP = kPairMfma ? kSqrtParts<D> : 1;
+  short4_t sqid[kSqP];
+  if constexpr (kPairMfma) {
+    uint16_t sq[2];
+    sqrt_d_parts<T>(a.sqrt_d, sq);
+#pragma unroll
+    for (int u = 0; u < kSqP; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sqid[u][e] = (4 * g + e == col) ? (short)sq[u] : (short)0;
   }
   // bf16: the n-sum of dpair adds the fp32 dS (the bf16-rounded dS, 2^-9
   // relative, summed over N slices reaches the gradient tolerance where a
@@ -355,8 +375,9 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
         reg_touch(o.m[hb]);
       }
     };
-    // S^T = K Q^T + sqrt(D) mask and dP^T = V dO^T - delta of one step
-    auto products = [&](const StepOps& o, floatx4(&sv)[2], floatx4(&dv)[2]) {
+    // S^T = K Q^T + sqrt(D) mask (+ sqrt(D) pair, bf16) and dP^T = V dO^T - delta of step st
+    auto products = [&](auto stc, const StepOps& o, floatx4(&sv)[2], floatx4(&dv)[2]) {
+      constexpr int st = decltype(stc)::value;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         floatx4 acc = __builtin_bit_cast(floatx4, o.m[hb]), accd = ndel;
@@ -364,6 +385,11 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
         for (int s = 0; s < KS32; ++s) {
           acc = T::mfma16(__builtin_bit_cast(short8_t, o.k[hb][s]), qop[s], acc);
           accd = T::mfma16(__builtin_bit_cast(short8_t, o.v[hb][s]), gop[s], accd);
+        }
+        if constexpr (kPairMfma) {
+          mfma_acc_handoff(acc);
+#pragma unroll
+          for (int u = 0; u < kSqP; ++u) acc = T::mfma16k16(sqid[u], __builtin_bit_cast(short4_t, pbias[2 * st + hb]), acc);
         }
         sv[hb] = acc;
         dv[hb] = accd;
@@ -378,7 +404,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     load_ops(std::integral_constant<int, 0>{}, ops);
     lgkm_wait<0>();
     touch_ops(ops);
-    products(ops, sc[0], dp[0]);
+    products(std::integral_constant<int, 0>{}, ops, sc[0], dp[0]);
     if constexpr (NSTEP > 1) load_ops(std::integral_constant<int, 1>{}, ops);
     static_for<0, NSTEP>([&](auto stc) {
       constexpr int st = decltype(stc)::value;
@@ -390,7 +416,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
       if constexpr (st + 1 < NSTEP) {
         lgkm_wait<0>();
         touch_ops(ops);
-        products(ops, sc[cur ^ 1], dp[cur ^ 1]);
+        products(std::integral_constant<int, st + 1>{}, ops, sc[cur ^ 1], dp[cur ^ 1]);
         if constexpr (st + 2 < NSTEP) load_ops(std::integral_constant<int, st + 2>{}, ops);
       }
       if (32 * st < lkl) {
@@ -409,7 +435,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float x;
-            if constexpr (HAS_PAIR) {
+            if constexpr (HAS_PAIR && !kPairMfma) {
               const uint32_t w = pbias[blk][r / 2];
               const float sv = (r & 1) ? T::fma_mix_hi(sc[cur][hb][r], scale, w) : T::fma_mix_lo(sc[cur][hb][r], scale, w);
               x = __builtin_fmaf(sv, kLog2e, nl);

@@ -141,6 +141,47 @@ struct BF16 {
   }
 };
 
+// ------------------------------------------------------------ bias by MFMA
+// bf16 has no mixed-precision FMA, so a VALU pair-bias add would widen each
+// value first; the bf16 forward and query-side backward add the bias inside
+// the score MFMA chain instead,
+// with an A operand that holds sqrt(D) on the diagonal of the block's keys
+// (the scores' accumulator holds sqrt(D) times each bias, as for the mask).
+// sqrt(D) is exact in 16 bits at D = 16 and 64; at D = 8 and 32 it is taken as
+// the dtype's rounding plus the rounding of the remainder, two products whose
+// sum is within 3e-7 relative (one value alone is off by 1.1e-4).  The
+// products are exact in fp32.
+template <int D>
+constexpr int kSqrtParts = (D == 16 || D == 64) ? 1 : 2;
+
+template <class T>
+__device__ __forceinline__ void sqrt_d_parts(float sqrt_d, uint16_t (&p)[2]) {
+  p[0] = T::from_f32(sqrt_d);
+  p[1] = T::from_f32(sqrt_d - T::to_f32(p[0]));
+}
+
+// Wait states between an MFMA result and its use as the accumulator input of an
+// MFMA of another opcode (a 16x16x32 score chain into the 16x16x16 bias
+// product).  The compiler inserts none when the accumulator registers overlap
+// exactly, as it may between two MFMAs of one opcode, but across the two
+// opcodes the result is not reliably there yet: without these the backward's
+// outputs differed from run to run on identical inputs (gfx950), with them
+// every run gave the same bits.  The asm takes the accumulator as an operand,
+// so the compiler cannot move either product past it.
+__device__ __forceinline__ void mfma_acc_handoff(floatx4& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc));
+}
+
+// bf16 pair-bias bits for such a product: -inf (and the NaNs of negative sign)
+// become the most negative finite value, whose product with sqrt(D) still
+// overflows to -inf in fp32 while the zeros off the diagonal give 0, not
+// 0 * inf = NaN.  One packed 16-bit minimum per two values.
+__device__ __forceinline__ uint32_t bf16x2_no_neg_inf(uint32_t w) {
+  using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
+  const u16x2 lim = {(unsigned short)0xFF7F, (unsigned short)0xFF7F};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, w), lim));
+}
+
 // ------------------------------------------------------------ lane helpers
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }

@@ -68,16 +68,6 @@ struct FwdShape {
   static constexpr int MB = (D + 31) / 32;        // 32-row blocks of O^T
 };
 
-// bf16 pair-bias bits for the bias product: -inf (and the NaNs of negative
-// sign) become the most negative finite value, whose product with the
-// diagonal's sqrt(D) still overflows to -inf in fp32 while the zeros off the
-// diagonal give 0, not 0 * inf = NaN.  One packed 16-bit minimum per two values.
-__device__ __forceinline__ uint32_t bf16x2_no_neg_inf(uint32_t w) {
-  using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
-  const u16x2 lim = {(unsigned short)0xFF7F, (unsigned short)0xFF7F};
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, w), lim));
-}
-
 // Pair-bias values of one 32-key block, 16 per lane (query i, half), in one of
 // two orders.  kMfma: the B operand of the bias product, which adds the bias
 // to the S^T accumulator through the MFMA (an identity over the block's keys,
@@ -226,26 +216,22 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
     }
   }
 
-  // A operands of the bias product: sqrt(D) on the diagonal of the block's
-  // keys, so the product adds sqrt(D) pair[i][j] to S^T[j][i] as the mask term
-  // adds sqrt(D) mask[j]; for k-step s, lane (key m, half) holds it at position
-  // m - 16 s - 8 half when that lies in 0..7.  sqrt(D) is exact in 16 bits at
-  // D = 16 and 64; at D = 8 and 32 it is taken as the dtype's rounding plus the
-  // rounding of the remainder, a second product (one 16-bit value alone is off
-  // by 1.1e-4 relative; the two together by under 3e-7).  The products are
-  // exact in fp32, the sums are the accumulator's.
-  constexpr int kSqParts = (D == 16 || D == 64) ? 1 : 2;
+  // A operands of the bias product (bf16): the parts of sqrt(D) on the
+  // diagonal of the block's keys, so the product adds sqrt(D) pair[i][j] to
+  // S^T[j][i] as the mask term adds sqrt(D) mask[j]; for k-step s, lane
+  // (key m, half) holds it at position m - 16 s - 8 half when that lies in 0..7
+  constexpr int kSqParts = kSqrtParts<D>;
   short8_t pid[kPairMfma ? kSqParts : 1][2];
   if constexpr (kPairMfma) {
-    const uint16_t hi = T::from_f32(a.sqrt_d);
-    const uint16_t lo = T::from_f32(a.sqrt_d - T::to_f32(hi));
+    uint16_t sq[2];
+    sqrt_d_parts<T>(a.sqrt_d, sq);
     const int m = lane & 31;
 #pragma unroll
     for (int u = 0; u < kSqParts; ++u)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pid[u][s2][e] = (m == 16 * s2 + 8 * half + e) ? (short)(u ? lo : hi) : (short)0;
+        for (int e = 0; e < 8; ++e) pid[u][s2][e] = (m == 16 * s2 + 8 * half + e) ? (short)sq[u] : (short)0;
   }
   // scale to log2 units of an accumulator that holds every term of the score
   const float c1 = a.scale * kLog2e;

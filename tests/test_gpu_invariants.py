@@ -4,7 +4,8 @@ error behaviour on a real device.
 * masked keys: changing K and V at keys whose mask is -1e9 changes no output
   bit; dK, dV and dmask are exactly zero there (P is exactly zero at those keys);
 * determinism: two runs give the same bits (every path, rows longer than one
-  key tile included: every reduction runs in a fixed order, no atomics);
+  key tile included: every reduction runs in a fixed order, no atomics), and
+  repeated backward calls at sizes that fill the device do too;
 * inference forward (no lse kept): the same output bits as the forward that
   keeps the lse, through the C ABI and through the no-grad Python call;
 * coverage: outputs pre-filled with NaN come back finite (every element written);
@@ -114,6 +115,35 @@ def test_every_output_written_guards_intact_deterministic(cfg):
     _assert_guards(b, 0x00)
     for name in _outputs(a):
         assert torch.equal(_outputs(a)[name], _outputs(b)[name]), f"{name} differs between two runs"
+
+
+REPEAT = [
+    I.custom("rep_l640_d32_bf16", 2, 8, 640, 2, 32, "bf16", 0.05, 1.0, 52),
+    I.custom("rep_l128_d64_bf16", 1, 8, 128, 2, 64, "bf16", 0.05, 1.0, 54),
+    I.custom("rep_l256_d32", 1, 16, 256, 4, 32, "fp16", 0.05, 1.0, 55),
+]
+
+
+@pytest.mark.parametrize("cfg", REPEAT, ids=[c.name for c in REPEAT])
+def test_backward_bits_repeat(cfg):
+    """Several backward calls on the same inputs give the same bits, at sizes that
+    keep every CU busy (a product that reads an accumulator before it is written
+    shows up here as outputs that change from call to call)."""
+    from evoformer_biased_attention_amd.attention import attn_bwd, attn_fwd
+
+    print(f"case repeat {cfg.name} shape={cfg.shape} dtype={cfg.dtype}", flush=True)
+    _, x = _inputs(cfg)
+    out, lse = attn_fwd(x["q"], x["k"], x["v"], x["mask_bias"], x["pair_bias"])
+    ref = None
+    for rep in range(4):
+        g = attn_bwd(x["q"], x["k"], x["v"], x["mask_bias"], x["pair_bias"], out, lse, x["dout"])
+        torch.cuda.synchronize()
+        got = {k: g[k].clone() for k in ("dq", "dk", "dv", "dmask", "dpair")}
+        if ref is None:
+            ref = got
+            continue
+        for k in ref:
+            assert torch.equal(got[k], ref[k]), f"{k} differs on call {rep}"
 
 
 @pytest.mark.parametrize("cfg", CASES[:4] + [CASES[5]], ids=[c.name for c in CASES[:4] + [CASES[5]]])
