@@ -162,14 +162,15 @@ __device__ __forceinline__ void sqrt_d_parts(float sqrt_d, uint16_t (&p)[2]) {
 
 // Wait states between an MFMA result and its use as the accumulator input of an
 // MFMA of another opcode (a 16x16x32 score chain into the 16x16x16 bias
-// product).  The compiler inserts none when the accumulator registers overlap
-// exactly, as it may between two MFMAs of one opcode, but across the two
-// opcodes the result is not reliably there yet: without these the backward's
-// outputs differed from run to run on identical inputs (gfx950), with them
-// every run gave the same bits.  The asm takes the accumulator as an operand,
-// so the compiler cannot move either product past it.
+// product, both 4 passes).  The compiler inserts none when the accumulator
+// registers overlap exactly, as it may between two MFMAs of one opcode, but
+// across the two opcodes the result is not reliably there yet.  Measured on
+// gfx950: with no wait states the backward's outputs changed from call to call
+// on identical inputs; with 4, 6, 8 or 16 every call gave the same bits, equal
+// across the four.  6 are used (the passes plus two).  The asm takes the
+// accumulator as an operand, so the compiler cannot move either product past it.
 __device__ __forceinline__ void mfma_acc_handoff(floatx4& acc) {
-  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc));
+  asm volatile("s_nop 5" : "+v"(acc));
 }
 
 // bf16 pair-bias bits for such a product: -inf (and the NaNs of negative sign)
