@@ -27,8 +27,9 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
-// -1 unknown, 0 not gfx950, 1 gfx950
+// -1 unknown, 0 not gfx950, 1 gfx950; and the device's compute units
 int g_dev_ok[kMaxDevices];
+int g_dev_cus[kMaxDevices];
 std::once_flag g_dev_once[kMaxDevices];
 
 bool device_is_gfx950(int dev) {
@@ -36,12 +37,17 @@ bool device_is_gfx950(int dev) {
   std::call_once(g_dev_once[dev], [dev] {
     hipDeviceProp_t prop;
     g_dev_ok[dev] = 0;
+    g_dev_cus[dev] = 0;
     if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
       g_dev_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 0;
+      g_dev_cus[dev] = prop.multiProcessorCount;
     }
   });
   return g_dev_ok[dev] == 1;
 }
+
+// compute units of a device that passed device_is_gfx950
+int device_cus(int dev) { return (dev >= 0 && dev < kMaxDevices) ? g_dev_cus[dev] : 0; }
 
 // ------------------------------------------------ static backward scratch
 //
@@ -482,6 +488,7 @@ evo_status_t evo_attn_fwd_strided(const void* q, const void* k, const void* v, c
   a.G = plan_fwd_group(s);
   a.scale = (float)(1.0 / std::sqrt((double)s.D));
   a.sqrt_d = (float)std::sqrt((double)s.D);
+  a.ncu = device_cus(dev);
   hipError_t e = evo::launch_fwd(a, (int)s.D, dtype == EVO_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? EVO_OK : EVO_ERR_LAUNCH;
 }

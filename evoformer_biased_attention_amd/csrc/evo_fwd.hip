@@ -144,8 +144,39 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
   int rest = wg / H;
   const int it = rest % a.i_tiles;
   rest /= a.i_tiles;
-  const int ng = rest % a.n_groups;
-  const int b = rest / a.n_groups;
+  int ng = rest % a.n_groups;
+  int b = rest / a.n_groups;
+  if (a.balance) {
+    // (b, n-group) by balanced_unit_rank over the batch entries ranked by the
+    // live 32-key blocks of their slice 0, a block counted when its first key
+    // is not -inf (padding at the end of a row: the blocks the kernel
+    // computes); ties keep the order of b.  One load per lane (entry, block),
+    // one ballot; every wave takes the same decision on its own.
+    const int nb = (L + 31) / 32;  // a.B * nb <= 64 (checked by the launcher)
+    bool live = false;
+    if (lane < a.B * nb) live = a.mask[(size_t)(lane / nb) * N * L + (lane % nb) * 32] != T::kNegInfBits;
+    const uint64_t bits = __builtin_amdgcn_ballot_w64(live);
+    const uint64_t seg = nb >= 64 ? ~0ull : ((1ull << nb) - 1);
+    const int unit = H * a.i_tiles;
+    const int r = balanced_unit_rank(wg, (int)gridDim.x / 8, unit, a.B * a.n_groups);
+    const int want = r / a.n_groups;  // rank of the batch entry among all
+    int cost[kBalanceMaxB];
+#pragma unroll
+    for (int bb = 0; bb < kBalanceMaxB; ++bb) {
+      const uint64_t m = bb < a.B ? (bits >> (bb * nb)) & seg : 0ull;
+      cost[bb] = bb < a.B ? (m ? 64 - (int)__builtin_clzll(m) : 0) : -1;
+    }
+    int pick = 0;
+#pragma unroll
+    for (int bb = 0; bb < kBalanceMaxB; ++bb) {
+      int rank = 0;
+#pragma unroll
+      for (int o = 0; o < kBalanceMaxB; ++o) rank += (cost[o] > cost[bb] || (cost[o] == cost[bb] && o < bb)) ? 1 : 0;
+      if (bb < a.B && rank == want) pick = bb;
+    }
+    b = pick;
+    ng = r % a.n_groups;
+  }
 
   const int i = it * kFwdRows + wave * 32 + (lane & 31);
   const bool i_valid = i < L;
@@ -715,8 +746,18 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
 // ------------------------------------------------------------------ launch
 
 template <class T, int D, bool HM, bool HP>
-static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+static hipError_t launch_fwd_t(const FwdArgs& a_in, hipStream_t stream) {
+  FwdArgs a = a_in;
   const int grid = a.B * a.H * a.i_tiles * a.n_groups;
+  // the balanced work order: a mask to rank the batch entries by (one wave's
+  // lanes cover every entry's blocks), two workgroups per CU in one round (not
+  // the three-wave tiles), and units that split evenly over the XCDs' halves
+  a.balance = 0;
+  if (HM && a.mask != nullptr && !kFwdThreeWaves<D, HP> && a.B >= 2 && a.B <= kBalanceMaxB &&
+      a.B * ((a.L + 31) / 32) <= 64 && a.ncu > 0 && grid == 2 * a.ncu && grid % 8 == 0) {
+    const int per = grid / 8, unit = a.H * a.i_tiles;
+    if (per % (2 * unit) == 0) a.balance = 1;
+  }
   prof_begin(K_FWD, stream);
   bool resident = false;  // the pair bias held for the whole row (rows of one key tile)
   if constexpr (HP) resident = a.L <= KVTile<D>::CH;

@@ -23,6 +23,8 @@ struct FwdArgs {
   int i_tiles;   // query tiles per slice
   float scale;   // 1/sqrt(D)
   float sqrt_d;  // sqrt(D) in fp32 (the mask enters the score accumulator pre-multiplied by it)
+  int ncu;       // compute units of the device
+  int balance;   // 1: batch entries ordered by live length, long paired with short on each CU
 };
 
 struct BwdArgs {
@@ -77,6 +79,22 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
   const int slot = id / kXcd;
   return xcd * per + slot;
 }
+
+// Work order for batches whose entries differ in live length (padding masked
+// with -inf).  A grid of exactly two workgroups per CU runs in one round, and
+// xcd_remap gives XCD x the logical workgroups [x per, (x + 1) per), of which
+// local slots j and j + per / 2 share a CU.  Work units (the `unit`
+// consecutive workgroups of one (b, n-group)) are ranked from the costliest
+// down; XCD x's first half of unit slots takes ranks x half .. x half + half - 1
+// from the top, its second half the same count from the bottom, so each CU
+// holds one costly and one cheap unit.  A bijection from logical unit slots to
+// ranks when per is a multiple of 2 unit and the grid is 8 per.
+__host__ __device__ inline int balanced_unit_rank(int lg, int per, int unit, int total_units) {
+  const int x = lg / per, u = (lg % per) / unit;
+  const int half = per / unit / 2;
+  return u < half ? x * half + u : total_units - 1 - (x * half + (u - half));
+}
+constexpr int kBalanceMaxB = 8;  // batch entries ranked by one workgroup
 
 hipError_t launch_fwd(FwdArgs a, int D, bool bf16, hipStream_t stream);
 hipError_t launch_bwd(BwdArgs a, int D, bool bf16, hipStream_t stream);

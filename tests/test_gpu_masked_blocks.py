@@ -9,9 +9,9 @@ paths run: padded batches (fp16, where -1e9 overflows to -inf, and bf16 with an
 explicit -inf), whole key tiles past a row's padding, interior blocks of -inf
 keys (computed, and exact either way), a whole slice with every key masked
 (O = 0, lse = -inf, zero gradients), rows of one and of several key tiles,
-D = 8, 16, 32 and 64, with and without the pair bias, and -inf entries in the
-pair bias itself.  Tolerances and the comparison are those of the other parity
-tests.
+D = 8, 16, 32 and 64, with and without the pair bias, -inf entries in the
+pair bias itself, and batches whose entries the forward reorders by live length.
+Tolerances and the comparison are those of the other parity tests.
 """
 import numpy as np
 import pytest
@@ -165,3 +165,24 @@ def test_parity_pair_bias_neg_inf(cfg):
     assert not bool(res["dq"][:, :, i_dead, 0].any()), "dQ of that row"
     assert not bool(res["dk"][:, :, j_dead, 1].any()) and not bool(res["dv"][:, :, j_dead, 1].any()), \
         "dK, dV of the key with every pair entry -inf"
+
+
+BALANCED = [
+    I.custom("balanced_fp16_unsorted", 4, 64, 256, 4, 32, "fp16", 0.05, 1.0, 81, key_lengths=(96, 256, 160, 200)),
+    I.custom("balanced_bf16_inf_unsorted", 4, 64, 256, 4, 32, "bf16", 0.05, 1.0, 82, key_lengths=(200, 64, 256, 130),
+             mask_value=NEG_INF),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cfg", BALANCED, ids=[c.name for c in BALANCED])
+def test_parity_balanced_forward_order(cfg):
+    """Batch entries of different live lengths, in an order that is not sorted by
+    length, at a size whose forward grid is one round of two workgroups per CU:
+    the forward takes the entries in the order of their live blocks, pairing long
+    with short work on each CU.  Every element of every output against the oracle."""
+    print(f"case balanced order {cfg.name} shape={cfg.shape} dtype={cfg.dtype} lengths={cfg.key_lengths}",
+          flush=True)
+    bits = I.make_inputs(cfg)
+    res = _run_gpu(cfg, bits)
+    _compare(cfg, bits, res)
