@@ -206,13 +206,14 @@ int plan_fwd_group(const Shape& s) {
 int64_t key_tile(int64_t D) { return D == 64 ? 128 : 256; }
 
 // slices per bwd_q3 / bwd_kv3 workgroup (also the dpair partial count
-// divisor).  A workgroup takes 128 rows and one key tile; one runs per CU
-// (256 CUs).  The group count k is the smallest within 3% of the minimum of
+// divisor).  A workgroup takes 128 rows and one key tile (all key tiles
+// without a pair bias); one runs per CU (256 CUs).  The group count k is the smallest within 3% of the minimum of
 // (rounds of workgroups) x (slices per workgroup): fewer groups mean fewer
 // dpair partials and fewer per-workgroup set-ups.
 int plan_bwdq_group(const Shape& s, bool has_pair) {
   const int64_t jtiles = (s.L + key_tile(s.D) - 1) / key_tile(s.D);
-  const int64_t per_group = s.B * s.H * ((s.L + 127) / 128) * jtiles;
+  // without a pair bias a workgroup walks every key tile of its slices
+  const int64_t per_group = s.B * s.H * ((s.L + 127) / 128) * (has_pair ? jtiles : 1);
   const int64_t kmax = s.N < 4096 ? s.N : 4096;
   auto cost = [&](int64_t k) { return ((per_group * k + 255) / 256) * ((s.N + k - 1) / k); };
   int64_t best_t = INT64_MAX;
@@ -221,9 +222,11 @@ int plan_bwdq_group(const Shape& s, bool has_pair) {
   while (k < kmax && cost(k) * 100 > best_t * 103) ++k;
   int64_t g = (s.N + k - 1) / k;
   // rows longer than one key tile without a pair bias (no dpair partials to
-  // multiply): groups of at most 24 slices run in more, shorter rounds
-  // (measured on MI355X at (1,384,512,8,32): 374 -> 351 us)
-  if (jtiles > 1 && !has_pair && g > 24) g = 24;
+  // multiply; a workgroup walks all key tiles of its slices): at most 24 key
+  // tiles per workgroup, so the grid runs in more, shorter rounds (measured on
+  // MI355X at (1,384,512,8,32): bwd_q3 293 us at 24, 296 at 48, 304 at 96)
+  constexpr int64_t kMaxTilesPerGroup = 24;
+  if (jtiles > 1 && !has_pair && g * jtiles > kMaxTilesPerGroup) g = std::max<int64_t>(1, kMaxTilesPerGroup / jtiles);
   return (int)g;
 }
 
@@ -264,7 +267,9 @@ BwdQPlan plan_bwdq(const Shape& s, bool has_pair, size_t budget) {
   const int64_t jtiles = (s.L + key_tile(s.D) - 1) / key_tile(s.D);
   const int64_t g1 = plan_bwdq_group(s, has_pair);
   const int64_t k1 = (s.N + g1 - 1) / g1;
-  if (jtiles == 1) return {(int)g1, (int)k1, (int)s.N};
+  // rows of one key tile, and longer rows without a pair bias (a workgroup
+  // walks all key tiles and keeps dQ in registers): no partials, one chunk
+  if (jtiles == 1 || !has_pair) return {(int)g1, (int)k1, (int)s.N};
   const size_t dq_slice = (size_t)jtiles * s.B * s.L * s.H * s.D * sizeof(float);
   const size_t slot = has_pair ? (size_t)s.B * s.H * s.L * s.L * sizeof(float) : 0;
   auto bytes = [&](int64_t nc, int64_t k) { return al256((size_t)nc * dq_slice) + al256((size_t)k * slot); };
@@ -338,10 +343,10 @@ WsLayout ws_layout(const Shape& s, bool has_mask, bool has_pair, size_t budget) 
     off += al256(per * (size_t)w.ngq);
   }
   // fp32 partials of dQ of one chunk of slices, one per key tile, when a row
-  // spans several tiles
+  // spans several tiles and the query side splits it by key tile (with a pair bias)
   w.dq_part = (size_t)-1;
   const int64_t jtiles = (s.L + key_tile(s.D) - 1) / key_tile(s.D);
-  if (jtiles > 1) {
+  if (jtiles > 1 && has_pair) {
     w.dq_part = off;
     off += al256((size_t)jtiles * s.B * w.nc * s.L * s.H * s.D * sizeof(float));
   }

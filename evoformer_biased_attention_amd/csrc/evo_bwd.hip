@@ -141,6 +141,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const hipError_t e = launch_bwd_tile(a, D, bf16, st);
     if (e != hipSuccess) return e;
     fin(a, n_pair, n_mask, 0);
+  } else if (!HP) {
+    // no pair bias: bwd_q3 walks every key tile of its slices with dQ in
+    // registers (no partials), then bwd_kv3 over query tiles (it reads delta)
+    // and the sums of the dmask partials
+    hipError_t e = launch_bwd_q_split(a, D, bf16, 2, st);
+    if (e != hipSuccess) return e;
+    if ((e = launch_bwd_q_split(a, D, bf16, 1, st)) != hipSuccess) return e;
+    fin(a, 0, n_mask, 0);
   } else {
     // per chunk of slices: bwd_q3 over its key tiles (dQ partials, delta,
     // dpair slot sums), then the sum of its dQ partials; after the last

@@ -126,13 +126,18 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   int rest = wg / H;
   const int it = rest % itiles;
   rest /= itiles;
-  // rows longer than one key tile: each workgroup takes one key tile and
-  // leaves an fp32 partial of dQ, summed over the tiles by bwd_fin
+  // rows longer than one key tile: with SPLIT each workgroup takes one key
+  // tile and leaves an fp32 partial of dQ, summed over the tiles by bwd_fin
+  // (the dpair block of a key tile stays in registers over the slices).
+  // Without a pair bias there is no dpair to keep: one workgroup walks every
+  // key tile of each slice in turn (KLOOP) and dQ stays in registers.
+  constexpr bool KLOOP = !SPLIT && !HAS_PAIR;
   const int jtiles = SPLIT ? (L + TL::CH - 1) / TL::CH : 1;
   const int jt = SPLIT ? rest % jtiles : 0;
   if constexpr (SPLIT) rest /= jtiles;
+  const int kjt = KLOOP ? (L + TL::CH - 1) / TL::CH : 1;  // key tiles walked per slice
   const int kc0 = jt * TL::CH;
-  const int lk = L - kc0;  // keys of the row from this tile on
+  const int lk = L - kc0;  // keys of the row from this tile on (the first step's tile with KLOOP)
   const int ng = rest % a.n_groups_q;
   const int b = rest / a.n_groups_q;
   const int i = it * kRows + wave * 16 + col;
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   float lse_nx = 0.f;
   uint32_t mraw = 0;
   const bool mask_thread = tid < TL::CH;
-  auto load_rows = [&](int n) {
+  auto load_rows = [&](int n) {  // Q, dO, O rows and the lse of slice n
     const int64_t row = b * a.sB + n * a.sN + ic * a.sL + h * D;  // element offset of the lane's row
 #pragma unroll
     for (int s = 0; s < KS32; ++s) {
@@ -214,11 +219,15 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
       onx[s] = ov;
     }
     lse_nx = a.lse[(((size_t)b * N + n) * H + h) * L + ic];
-    if (mask_thread) mraw = a.mask ? a.mask[((size_t)b * N + n) * L + min(kc0 + tid, L - 1)] : 0u;
   };
-  auto store_mask = [&](int buf) {
+  // the mask row of slice n for the key tile from key kt0 on
+  auto load_mask = [&](int n, int kt0) {
+    if (mask_thread) mraw = a.mask ? a.mask[((size_t)b * N + n) * L + min(kt0 + tid, L - 1)] : 0u;
+  };
+  // ltk: keys of the row from that tile on
+  auto store_mask = [&](int buf, int ltk) {
     if (mask_thread) {  // whole waves: CH is a multiple of 64
-      const float mv = (tid < lk) ? T::to_f32((uint16_t)mraw) * a.sqrt_d : kNegInf;
+      const float mv = (tid < ltk) ? T::to_f32((uint16_t)mraw) * a.sqrt_d : kNegInf;
       smk[buf][tid] = mv;
       const uint64_t live = __builtin_amdgcn_ballot_w64(mv != kNegInf);
       if (lane == 0) slive[buf][wave] = live ? 64 * wave + 64 - (int)__builtin_clzll(live) : 0;
@@ -291,8 +300,9 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
 
   if (ntiles > 0) {
     load_rows(n_begin);
+    load_mask(n_begin, kc0);
     issue_tile<D, NT>(smem, slice_ptr(a.k, n_begin), slice_ptr(a.v, n_begin), coff, wave);
-    store_mask(0);
+    store_mask(0, lk);
     vm_wait_all();
     take_rows(n_begin);
   }
@@ -303,18 +313,30 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   // one key tile measured faster with the plain barrier and the rows taken
   // after it (A/B on one device: bwd_q3 -4% at L = 256, +10% with SPLIT at
   // L = 768).
-  for (int t = 0; t < ntiles; ++t) {
-    const int n = n_begin + t;
+  // Steps: (slice, key tile) pairs, the key tiles of a slice in turn (one per
+  // slice unless KLOOP); dQ accumulates over a slice's key tiles.
+  const int nsteps = ntiles * kjt;
+  floatx4 dq[MB];
+  for (int t = 0; t < nsteps; ++t) {
+    const int n = n_begin + t / kjt;
+    const int jts = t % kjt;  // the step's key tile (0 unless KLOOP)
+    const int lks = lk - jts * TL::CH;
+    const int t1 = t + 1, jt1 = t1 % kjt;  // the next step
+    const int n1 = n_begin + t1 / kjt;
     if constexpr (SPLIT) {
       lds_barrier();
     } else {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (t > 0) take_rows(n);
+      if (t > 0 && jts == 0) take_rows(n);
     }
-    if (t + 1 < ntiles) {
-      issue_tile<D, NT>(smem + ((t + 1) & 1) * TL::BUF_BYTES, slice_ptr(a.k, n + 1), slice_ptr(a.v, n + 1), coff, wave);
-      load_rows(n + 1);
+    if (t1 < nsteps) {
+      if constexpr (KLOOP) {
+        if (kjt > 1) tile_chunk_offsets<D, NT>(coff, jt1 * TL::CH, L, a.sL, h, wave, lane);
+      }
+      issue_tile<D, NT>(smem + (t1 & 1) * TL::BUF_BYTES, slice_ptr(a.k, n1), slice_ptr(a.v, n1), coff, wave);
+      if (jt1 == 0) load_rows(n1);
+      load_mask(n1, kc0 + jt1 * TL::CH);
     }
     const uint8_t* kb = smem + (t & 1) * TL::BUF_BYTES;
     const uint8_t* vb = kb + TL::KCH * 16;
@@ -325,7 +347,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
       const u32x4 lv = *reinterpret_cast<const u32x4*>(&slive[t & 1][0]);
       const int le = TL::CH > 128 ? max(max((int)lv[0], (int)lv[1]), max((int)lv[2], (int)lv[3]))
                                   : max((int)lv[0], (int)lv[1]);
-      lkl = min(lk, __builtin_amdgcn_readfirstlane(le));
+      lkl = min(lks, __builtin_amdgcn_readfirstlane(le));
     }
     // Row (key) 16 blk + col of a tile: the swizzle depends on col only, so a
     // block's operands sit at a fixed offset from the lane's base address.
@@ -396,9 +418,10 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
       }
     };
 
-    floatx4 dq[MB];
+    if (jts == 0) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) dq[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int mb = 0; mb < MB; ++mb) dq[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
     floatx4 sc[2][2], dp[2][2];
     StepOps ops;
     load_ops(std::integral_constant<int, 0>{}, ops);
@@ -471,13 +494,13 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
         for (int mb = 0; mb < MB; ++mb) dq[mb] = T::mfma16(cat4(kt[2 * mb], kt[2 * mb + 1]), dsw, dq[mb]);
       }
     });
-    vm_wait_all();  // the next slice's copies and row loads
-    if (t + 1 < ntiles) {
-      store_mask((t + 1) & 1);  // its buffer was last read during slice t-1
+    vm_wait_all();  // the next step's copies and loads
+    if (t1 < nsteps) {
+      store_mask(t1 & 1, lk - jt1 * TL::CH);  // its buffer was last read during step t-1
       if constexpr (SPLIT) take_rows(n + 1);
     }
-    // ---- dQ = scale * dQ^T: lane holds d = 16 mb + 4 g + 0..3 of query i
-    if (i_valid) {
+    // ---- dQ = scale * dQ^T (after a slice's last key tile): lane holds d = 16 mb + 4 g + 0..3 of query i
+    if (i_valid && jts == kjt - 1) {
       // dense row index of the fp32 partials (slices of the chunk)
       const size_t row = (((size_t)b * a.q_nc + (n - a.q_n0)) * L + i) * H + h;
       const int64_t qoff = b * a.sB + n * a.sN + i * a.sL + h * D;
@@ -975,6 +998,16 @@ static hipError_t launch_split_t(const BwdArgs& a, int part, hipStream_t st) {
     else
       hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, HP, false, true, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
     prof_end(K_BWD_Q, st);
+  } else if (part == 2) {
+    // no pair bias: bwd_q3 with every key tile of a slice in one workgroup
+    if constexpr (!HP) {
+      const int grid = a.B * a.H * ((a.L + kRows - 1) / kRows) * a.n_groups_q;
+      prof_begin(K_BWD_Q, st);
+      hipLaunchKernelGGL((evo_bwd_q3_kernel<T, D, false, false, false, NW>), dim3(grid), dim3(64 * NW), 0, st, a);
+      prof_end(K_BWD_Q, st);
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else {
     // key side over query tiles; it reads the delta bwd_q3 wrote
     const int gridk = a.B * a.H * ((a.L + kRows - 1) / kRows) * a.n_groups_k;

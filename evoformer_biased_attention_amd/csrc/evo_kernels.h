@@ -101,7 +101,8 @@ hipError_t launch_bwd(BwdArgs a, int D, bool bf16, hipStream_t stream);
 // backward for rows that fit one key tile (L <= 256, or 128 at D = 64): bwd_q3 then bwd_kv3
 hipError_t launch_bwd_tile(const BwdArgs& a, int D, bool bf16, hipStream_t stream);
 // longer rows: part 0 is bwd_q3 over one chunk of slices with one key tile
-// per workgroup (dQ left as fp32 partials), part 1 bwd_kv3 over query tiles
+// per workgroup (dQ left as fp32 partials), part 1 bwd_kv3 over query tiles,
+// part 2 (no pair bias) bwd_q3 with all key tiles of a slice in one workgroup
 hipError_t launch_bwd_q_split(const BwdArgs& a, int D, bool bf16, int part, hipStream_t stream);
 
 }  // namespace evo

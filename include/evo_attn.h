@@ -93,9 +93,11 @@ evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const voi
 /* Bytes of device workspace for evo_attn_bwd on this problem (0 on bad
  * arguments): fp32 delta and bias-gradient accumulators, the dpair partials of
  * the slice groups and, for rows longer than one key tile (L > 256, or > 128
- * at D = 64), the fp32 dQ partials of each key tile.  The backward fits its
- * plan to the workspace it is given: with less room it takes the slices of
- * long rows in chunks (more launches, smaller partials).  This size is that
+ * at D = 64) with a pair bias, the fp32 dQ partials of each key tile (without
+ * a pair bias the query side keeps dQ in registers over all key tiles and
+ * needs no partials).  The backward fits its plan to the workspace it is
+ * given: with less room it takes the slices of long rows in chunks (more
+ * launches, smaller partials).  This size is that
  * of the plan with at most 384 MiB of partials; evo_attn_bwd_workspace_bytes_within
  * gives the size for another bound on the partials (0: the least workspace
  * the backward accepts).  The workspace size is an input of the plan: the bias

@@ -135,7 +135,9 @@ def test_backward_plan_fits_the_workspace(shape, has_pair):
     """The backward fits its plan to the workspace: more room for the fp32
     partials never gives a smaller workspace, the partials stay within the
     budget whenever some plan fits it, the default is the plan for 384 MiB of
-    partials, and rows of one key tile do not depend on the budget at all."""
+    partials, and rows of one key tile, or longer rows without a pair bias
+    (dQ kept in registers over the key tiles, no partials), do not depend on
+    the budget at all."""
     dt = _lib.EVO_BF16
     within = lambda b: _lib.evo_attn_bwd_workspace_bytes_within(shape, dt, 1, has_pair, b)
     least = within(0)
@@ -146,7 +148,7 @@ def test_backward_plan_fits_the_workspace(shape, has_pair):
     assert _lib.evo_attn_bwd_workspace_bytes(shape, dt, 1, has_pair) == within(384 * MiB)
     B, N, L, H, D = shape
     jtiles = -(-L // (128 if D == 64 else 256))
-    if jtiles == 1:
+    if jtiles == 1 or not has_pair:
         assert len(set(sizes)) == 1
         return
     # the regions that do not depend on the plan: delta, dmask partials and

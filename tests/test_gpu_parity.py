@@ -97,12 +97,13 @@ def test_parity_triangle_full(part):
     compare_with_oracle(cfg, bits, res, parts=(part,))
 
 
-# rows longer than one key tile run with partial budgets below what their
-# fp32 partials take at once: bwd_q3 then goes over chunks of slices (the last
-# one ragged) and the dpair slots carry their sums from chunk to chunk
+# rows longer than one key tile with a pair bias run with partial budgets
+# below what their fp32 partials take at once: bwd_q3 then goes over chunks of
+# slices (the last one ragged) and the dpair slots carry their sums from chunk
+# to chunk (rows without a pair bias keep dQ in registers and never chunk)
 CHUNKED = [
     I.custom("chunked_b2_l640_d64_bf16", 2, 48, 640, 2, 64, "bf16", 0.05, 1.0, 31),
-    I.custom("chunked_l520_mask_only", 1, 120, 520, 8, 32, "fp16", 0.1, None, 32),
+    I.custom("chunked_l520_fp16", 1, 120, 520, 4, 32, "fp16", 0.1, 1.0, 32),
 ]
 
 
