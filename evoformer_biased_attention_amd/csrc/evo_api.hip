@@ -207,9 +207,10 @@ int64_t key_tile(int64_t D) { return D == 64 ? 128 : 256; }
 
 // slices per bwd_q3 / bwd_kv3 workgroup (also the dpair partial count
 // divisor).  A workgroup takes 128 rows and one key tile (all key tiles
-// without a pair bias); one runs per CU (256 CUs).  The group count k is the smallest within 3% of the minimum of
-// (rounds of workgroups) x (slices per workgroup): fewer groups mean fewer
-// dpair partials and fewer per-workgroup set-ups.
+// without a pair bias); one runs per CU (256 CUs).  The group count k is the
+// smallest within 3% of the minimum of (rounds of workgroups) x (slices per
+// workgroup): fewer groups mean fewer dpair partials and fewer per-workgroup
+// set-ups.
 int plan_bwdq_group(const Shape& s, bool has_pair) {
   const int64_t jtiles = (s.L + key_tile(s.D) - 1) / key_tile(s.D);
   // without a pair bias a workgroup walks every key tile of its slices
