@@ -20,6 +20,9 @@ CASES = [
     # rows longer than one key tile, planned in chunks (a 24 MiB partial
     # budget): bwd_q3 and bwd_fin launched once per chunk
     (I.custom("graph_chunked_l640_d64_bf16", 2, 24, 640, 2, 64, "bf16", 0.05, 1.0, 51), 24 << 20),
+    # rows longer than one key tile without a pair bias: bwd_q3 walks every
+    # key tile of its slices (no partials)
+    (I.custom("graph_l600_nopair_bf16", 1, 16, 600, 2, 32, "bf16", 0.05, None, 53), None),
 ]
 
 
@@ -33,7 +36,9 @@ def test_graph_replay_matches_eager(cfg, budget):
     out_e, lse_e = attn_fwd(q, k, v, m, p)
     g_e = attn_bwd(q, k, v, m, p, out_e, lse_e, do, partial_budget=budget)
     torch.cuda.synchronize()
-    ref = [t.clone() for t in (out_e, lse_e, g_e["dq"], g_e["dk"], g_e["dv"], g_e["dmask"], g_e["dpair"])]
+    # the outputs the call has (dmask, dpair are None without their bias)
+    ref = [t.clone() for t in (out_e, lse_e, g_e["dq"], g_e["dk"], g_e["dv"], g_e["dmask"], g_e["dpair"])
+           if t is not None]
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -45,7 +50,8 @@ def test_graph_replay_matches_eager(cfg, budget):
     with torch.cuda.graph(graph):
         out_g, lse_g = attn_fwd(q, k, v, m, p)
         g_g = attn_bwd(q, k, v, m, p, out_g, lse_g, do, partial_budget=budget)
-    got = (out_g, lse_g, g_g["dq"], g_g["dk"], g_g["dv"], g_g["dmask"], g_g["dpair"])
+    got = [t for t in (out_g, lse_g, g_g["dq"], g_g["dk"], g_g["dv"], g_g["dmask"], g_g["dpair"]) if t is not None]
+    assert len(got) == len(ref)
     for rep in range(4):
         graph.replay()
         torch.cuda.synchronize()

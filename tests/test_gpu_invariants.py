@@ -100,6 +100,7 @@ CASES = [
     I.custom("inv_l256_d8_bf16", 1, 4, 256, 4, 8, "bf16", 0.25, 1.0, 34),
     I.custom("inv_l300_bf16", 1, 2, 300, 2, 32, "bf16", 0.25, 1.0, 35),
     I.custom("inv_l520_d16", 1, 2, 520, 1, 16, "fp16", 0.25, 1.0, 36),
+    I.custom("inv_l600_nopair_bf16", 1, 3, 600, 2, 32, "bf16", 0.25, None, 37),
 ]
 
 
