@@ -362,7 +362,13 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
     }
   };
 
+  // A resident pair bias means rows of one key tile: every tile is a whole
+  // slice, whose first block's PV product takes a zero accumulator input in
+  // place of a cleared O^T accumulator.
+  constexpr bool kOneChunk = RES > 0;
   floatx16 oacc[S::MB];
+#pragma unroll
+  for (int mb2 = 0; mb2 < S::MB; ++mb2) oacc[mb2] = floatx16{};
   // m_used: the row's exponent base in log2 units; the row sum in two chains
   float m_used = kNegInf, l_part = 0.f, l_part2 = 0.f;
 
@@ -580,14 +586,21 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
 #pragma unroll
     for (int k = 0; k < S::KSTEPS_D; ++k) reg_touch(kpre[k]);
     if constexpr (kMcBufs == 2) reg_touch(mpre);
+    // (a slice's first block: the first product starts from zero, and the
+    // accumulator's earlier contents, rescaled by 0 above, are not read)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int mb2 = 0; mb2 < S::MB; ++mb2)
         oacc[mb2] = T::mfma(cat4(vt[(t * S::MB + mb2) * 2], vt[(t * S::MB + mb2) * 2 + 1]),
-                            __builtin_bit_cast(short8_t, bop[t]), oacc[mb2]);
+                            __builtin_bit_cast(short8_t, bop[t]),
+                            (kOneChunk && jb == 0 && t == 0) ? floatx16{} : oacc[mb2]);
     }
   };
+
+  // score accumulators and the mask terms of a tile's blocks (every block's are
+  // written before they are read; cleared once, so they always hold values)
+  floatx16 sacc[2], mcb[2] = {floatx16{}, floatx16{}};
 
   // ---- pipeline: tile t computes from buffer t&1 while tile t+1 streams into the other
   if (ntiles > 0) {
@@ -608,8 +621,10 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
     const int kc0 = c * TL::CH;
     lds_barrier();  // everyone's copies of tile t are done; everyone has finished tile t-1
     if (c == 0) {
+      if constexpr (!kOneChunk) {
 #pragma unroll
-      for (int mb2 = 0; mb2 < S::MB; ++mb2) oacc[mb2] = floatx16{};
+        for (int mb2 = 0; mb2 < S::MB; ++mb2) oacc[mb2] = floatx16{};
+      }
       m_used = kNegInf;
       l_part = 0.f;
       l_part2 = 0.f;
@@ -640,6 +655,13 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
                                   : max((int)lv[0], (int)lv[1]);
       nblk = min(nblk, (__builtin_amdgcn_readfirstlane(le) + 31) / 32);
     }
+    if constexpr (kOneChunk) {
+      // a slice with no block to compute stores zeros from a cleared accumulator
+      if (nblk == 0) {
+#pragma unroll
+        for (int mb2 = 0; mb2 < S::MB; ++mb2) oacc[mb2] = floatx16{};
+      }
+    }
     {
       constexpr int NB = (RES > 0 && RES < TL::CH / 32) ? RES : TL::CH / 32;
       short8_t kreg[2][S::KSTEPS_D];
@@ -650,7 +672,6 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
       // it: -3% at (1,256,256,4,32)).  bf16 and D = 64, whose kernels are at
       // the register limit: block 0 in mcb[0] and every later block in mcb[1],
       // loaded by tracked reads.
-      floatx16 sacc[2], mcb[2] = {floatx16{}, floatx16{}};
       auto msel = [](int j) { return kMcBufs == 2 ? (j & 1) : (j == 0 ? 0 : 1); };
       const uint32_t bufa = lds_addr(buf);
       k_fetch(std::integral_constant<int, 0>{}, bufa, kreg[0]);
