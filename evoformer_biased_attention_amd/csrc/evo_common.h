@@ -194,13 +194,6 @@ __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u,
 __device__ __forceinline__ void xhalf_swap(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
-// The value lane l ^ 32 holds.
-__device__ __forceinline__ uint32_t xhalf_partner(uint32_t x) {
-  float a = __builtin_bit_cast(float, x), b = a;
-  xhalf_swap(a, b);  // lanes < 32 find the partner's value in b, lanes >= 32 in a
-  const bool lo = (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) < 32);
-  return __builtin_bit_cast(uint32_t, lo ? b : a);
-}
 __device__ __forceinline__ float xhalf_sum(float x) {
   float a = x, b = x;
   xhalf_swap(a, b);

@@ -727,33 +727,19 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
       const float l_tot = xhalf_sum(l_part + l_part2);
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       {
-        // lanes l and l^32 hold alternating runs of 4 columns of the same row;
-        // one exchange per pair of runs gives each lane 8 contiguous columns,
-        // stored as one 16-byte write
+        // lanes l and l^32 hold alternating runs of 4 columns of the same row
+        // (lane half h: columns 32 mb + 8 q + 4 h .. +3); each run is stored as
+        // one 8-byte write, the two halves' runs side by side in memory
         uint16_t* orow = a.out + b * a.sB + n * a.sN + ic * a.sL + h * D;
 #pragma unroll
         for (int mb2 = 0; mb2 < S::MB; ++mb2)
 #pragma unroll
-          for (int q = 0; q < 4; q += 2) {
-            uint32_t run[2][2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              run[u][0] = T::pack2(oacc[mb2][4 * (q + u)] * inv, oacc[mb2][4 * (q + u) + 1] * inv);
-              run[u][1] = T::pack2(oacc[mb2][4 * (q + u) + 2] * inv, oacc[mb2][4 * (q + u) + 3] * inv);
-            }
-            // half 0 keeps run q and receives the partner's run q; half 1 keeps
-            // run q+1 and receives the partner's run q+1
-            uint32_t snd0 = half ? run[0][0] : run[1][0];
-            uint32_t snd1 = half ? run[0][1] : run[1][1];
-            const uint32_t rcv0 = xhalf_partner(snd0), rcv1 = xhalf_partner(snd1);
-            u32x4 w;
-            if (half == 0) {
-              w = u32x4{run[0][0], run[0][1], rcv0, rcv1};
-            } else {
-              w = u32x4{rcv0, rcv1, run[1][0], run[1][1]};
-            }
-            const int d = 32 * mb2 + 8 * (q + half);
-            if (i_valid && d < D) *reinterpret_cast<u32x4*>(orow + d) = w;
+          for (int q = 0; q < 4; ++q) {
+            u32x2 w;
+            w[0] = T::pack2(oacc[mb2][4 * q] * inv, oacc[mb2][4 * q + 1] * inv);
+            w[1] = T::pack2(oacc[mb2][4 * q + 2] * inv, oacc[mb2][4 * q + 3] * inv);
+            const int d = 32 * mb2 + 8 * q + 4 * half;
+            if (i_valid && d < D) *reinterpret_cast<u32x2*>(orow + d) = w;
           }
         if (i_valid && half == 0 && a.lse != nullptr) {
           const float lse = (m_used == kNegInf || !(l_tot > 0.f)) ? kNegInf : __builtin_fmaf(m_used, kLn2, __logf(l_tot));
