@@ -493,6 +493,17 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) dq[mb] = T::mfma16(cat4(kt[2 * mb], kt[2 * mb + 1]), dsw, dq[mb]);
       }
+      // rows longer than one key tile: blocks 2 st and 2 st + 1 of the dpair
+      // slot are final after the group's last step reaches them, and their
+      // stores go out under the remaining steps instead of all at the end
+      // (A/B on MI355X: bwd_q3 -8% at (1,768,768,4,32); rows of one key tile
+      // measured the same or slower, and store at the end)
+      if constexpr (WANT_DPAIR && SPLIT) {
+        if (t == nsteps - 1) {
+          store_dpair(2 * st);
+          store_dpair(2 * st + 1);
+        }
+      }
     });
     vm_wait_all();  // the next step's copies and loads
     if (t1 < nsteps) {
@@ -522,7 +533,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     }
   }
 
-  if constexpr (WANT_DPAIR) {
+  if constexpr (WANT_DPAIR && !SPLIT) {
     if (ntiles > 0) {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) store_dpair(blk);
