@@ -74,11 +74,15 @@ struct FwdShape {
 // scaled by sqrt(D) as the mask term is, times the pair rows): position
 // 8 s + e holds pair[i][j0 + 16 s + 8 half + e].  Otherwise the S^T accumulator
 // order, for a bias added to the scores by the VALU: position 4 q + u holds
-// pair[i][j0 + 8 q + 4 half + u].  Columns >= L read zero (those keys are
-// masked to -inf by the mask term).  vec: L is a multiple of the run of
-// consecutive keys (8 or 4), so the runs are aligned vector loads.  The MFMA
-// order is that of bf16 and takes its -inf values out (bf16x2_no_neg_inf).
-template <bool kMfma>
+// pair[i][j0 + 8 q + 4 half + u].  vec: L is a multiple of the run of
+// consecutive keys (8 or 4), so the runs are aligned vector loads.
+// kSettle: columns >= L read zero and the MFMA order (that of bf16) takes its
+// -inf values out (bf16x2_no_neg_inf), which makes the caller wait for the
+// loads at once.  Without it the loaded values are left as they arrive, for
+// a caller that applies pair_no_neg_inf before the product: columns >= L then
+// hold finite values of the row's last keys, which the mask term turns into
+// -inf scores as it does for zeros.
+template <bool kMfma, bool kSettle = true>
 __device__ __forceinline__ void load_pair_ops(short8_t (&dst)[2], const uint16_t* prow, int j0, int L, int half,
                                               bool vec) {
   constexpr int G = kMfma ? 8 : 4;  // consecutive keys per run
@@ -89,29 +93,41 @@ __device__ __forceinline__ void load_pair_ops(short8_t (&dst)[2], const uint16_t
     if (vec) {  // uniform; j + G - 1 < L whenever j < L
       if constexpr (kMfma) {
         u32x4 v = *reinterpret_cast<const u32x4*>(prow + min(j, L - G));
-        if (j >= L) v = u32x4{0u, 0u, 0u, 0u};
+        if (kSettle && j >= L) v = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[4 * g + e] = v[e];
       } else {
         u32x2 v = *reinterpret_cast<const u32x2*>(prow + min(j, L - G));
-        if (j >= L) v = u32x2{0u, 0u};
+        if (kSettle && j >= L) v = u32x2{0u, 0u};
         w[2 * g] = v[0];
         w[2 * g + 1] = v[1];
       }
     } else {
       uint32_t t[G];
 #pragma unroll
-      for (int e = 0; e < G; ++e) t[e] = (j + e < L) ? (uint32_t)prow[min(j + e, L - 1)] : 0u;
+      for (int e = 0; e < G; ++e) t[e] = (!kSettle || j + e < L) ? (uint32_t)prow[min(j + e, L - 1)] : 0u;
 #pragma unroll
       for (int e = 0; e < G; e += 2) w[(g * G + e) / 2] = t[e] | (t[e + 1] << 16);
     }
   }
-  if constexpr (kMfma) {
+  if constexpr (kMfma && kSettle) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) w[e] = bf16x2_no_neg_inf(w[e]);
   }
 #pragma unroll
   for (int s = 0; s < 2; ++s) dst[s] = __builtin_bit_cast(short8_t, u32x4{w[4 * s], w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]});
+}
+
+// The -inf values of pair-bias operands in the MFMA order taken out in place
+// (the second half of load_pair_ops' settling, for operands loaded without it).
+__device__ __forceinline__ void pair_no_neg_inf(short8_t (&p)[2]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    u32x4 w = __builtin_bit_cast(u32x4, p[s]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = bf16x2_no_neg_inf(w[e]);
+    p[s] = __builtin_bit_cast(short8_t, w);
+  }
 }
 
 template <class T, int D, bool HAS_MASK, bool HAS_PAIR, int RES>
@@ -140,12 +156,32 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
   // are consecutive, so all heads and query tiles of a run of slices share
   // that XCD's L2 (the heads of a row are interleaved in memory)
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = wg % H;
-  int rest = wg / H;
-  const int it = rest % a.i_tiles;
-  rest /= a.i_tiles;
-  int ng = rest % a.n_groups;
-  int b = rest / a.n_groups;
+  int h, it, ng, b;
+  if constexpr (RES == 0 && HAS_PAIR) {
+    // a streamed pair bias (rows longer than one key tile) is re-read for
+    // every slice: (two heads, query tile, n-group) order instead, so that
+    // the workgroups one XCD runs at a time read the bias planes of two
+    // heads, which stay in its L2 (two heads share the cache lines of a Q,
+    // K, V row; measured on MI355X at (1,768,768,4,32): forward -6% against
+    // the order below, whose XCDs each read all heads' planes)
+    const int hp = (H % 2) == 0 ? 2 : 1;
+    int r = wg;
+    const int hl = r % hp;
+    r /= hp;
+    it = r % a.i_tiles;
+    r /= a.i_tiles;
+    ng = r % a.n_groups;
+    r /= a.n_groups;
+    h = (r % (H / hp)) * hp + hl;
+    b = r / (H / hp);
+  } else {
+    h = wg % H;
+    int rest = wg / H;
+    it = rest % a.i_tiles;
+    rest /= a.i_tiles;
+    ng = rest % a.n_groups;
+    b = rest / a.n_groups;
+  }
   if (a.balance) {
     // (b, n-group) by balanced_unit_rank over the batch entries ranked by the
     // live 32-key blocks of their slice 0, a block counted when its first key
@@ -602,8 +638,26 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
   // written before they are read; cleared once, so they always hold values)
   floatx16 sacc[2], mcb[2] = {floatx16{}, floatx16{}};
 
+  // Streamed pair bias (rows longer than one key tile): a ring of kRing
+  // blocks' values, block j in slot j % kRing, each loaded kRing - 1 blocks
+  // before the block that uses it (across tile boundaries: the pair bias
+  // does not depend on n).  Against loading a whole tile's bias at the top of
+  // the tile, this holds half the registers and takes no load latency at the
+  // start of a tile (measured on MI355X at (1,768,768,4,32): forward -25%).
+  constexpr bool kStream = RES == 0 && HAS_PAIR;
+  constexpr int kRing = 4;
+  short8_t pring[kStream ? kRing : 1][2];
+  // the next tile's copies go out in the middle of a streamed tile, after the
+  // bias loads of the blocks before it: waiting for those never waits for
+  // the copies, which have half a tile to complete
+  constexpr int kIssueAt = kStream ? TL::CH / 64 - 1 : 0;
+
   // ---- pipeline: tile t computes from buffer t&1 while tile t+1 streams into the other
   if (ntiles > 0) {
+    if constexpr (kStream) {
+#pragma unroll
+      for (int j = 0; j < kRing - 1; ++j) load_pair_ops<kPairMfma, false>(pring[j], prow, j * 32, L, half, pvec);
+    }
     issue_tile(0);
     load_mask(n_begin, 0);
     load_q(qnext, n_begin);
@@ -629,19 +683,17 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
       l_part = 0.f;
       l_part2 = 0.f;
     }
-    // streamed pair bias: this tile's blocks are loaded before the next tile's
-    // copies are issued, so waiting for them never waits for the prefetch
-    short8_t ptile[RES > 0 || !HAS_PAIR ? 1 : TL::CH / 32][2];
-    if constexpr (RES == 0 && HAS_PAIR) {
-#pragma unroll
-      for (int jb = 0; jb < TL::CH / 32; ++jb) load_pair_ops<kPairMfma>(ptile[jb], prow, kc0 + jb * 32, L, half, pvec);
-    }
-    if (t + 1 < ntiles) {
-      issue_tile(t + 1);
-      const int n1 = n_begin + (t + 1) / nchunks;
-      load_mask(n1, ((t + 1) % nchunks) * TL::CH);
-      if ((t + 1) % nchunks == 0) load_q(qnext, n1);
-    }
+    // the next tile's copies, mask row and Q rows
+    auto issue_next = [&]() {
+      if (t + 1 < ntiles) {
+        issue_tile(t + 1);
+        const int n1 = n_begin + (t + 1) / nchunks;
+        load_mask(n1, ((t + 1) % nchunks) * TL::CH);
+        if ((t + 1) % nchunks == 0) load_q(qnext, n1);
+      }
+    };
+    if constexpr (!kStream) issue_next();
+    const int kc0n = ((t + 1) % nchunks) * TL::CH;  // the next tile's first key
     const int tb = t & 1;
     const uint8_t* buf = smem + tb * TL::BUF_BYTES;
     // blocks of the tile, software-pipelined: while block jb is in its softmax,
@@ -691,17 +743,36 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
         if constexpr (RES > 0) {
           return pres[j < RES ? j : 0];
         } else {
-          return ptile[HAS_PAIR ? j : 0];
+          return pring[kStream ? j % kRing : 0];
         }
       };
+      // streamed bf16 bias: a block's -inf values are taken out just before its
+      // product, two blocks after its load (not at the load, which would wait
+      // for it there)
+      if constexpr (kStream && kPairMfma) pair_no_neg_inf(pring[0]);
       sacc[0] = qk_block(kreg[0], mcb[0], pops(std::integral_constant<int, 0>{}));
       static_for<0, NB>([&](auto jbc) {
         constexpr int jb = decltype(jbc)::value;
+        if constexpr (kStream) {
+          // block jb + kRing - 1 (of this tile or the next) into the slot
+          // block jb - 1 has finished with; loaded also past the tile's last
+          // live block, so that the next tile's first blocks are there
+          constexpr int jl = jb + kRing - 1;
+          if constexpr (jl < NB) {
+            load_pair_ops<kPairMfma, false>(pring[jl % kRing], prow, kc0 + jl * 32, L, half, pvec);
+          } else {
+            if (t + 1 < ntiles)
+              load_pair_ops<kPairMfma, false>(pring[jl % kRing], prow, kc0n + (jl - NB) * 32, L, half, pvec);
+          }
+          if constexpr (jb == kIssueAt) issue_next();
+        }
         if (jb < nblk) {
           if constexpr (jb + 1 < NB) {
-            if (jb + 1 < nblk)
+            if (jb + 1 < nblk) {
+              if constexpr (kStream && kPairMfma) pair_no_neg_inf(pring[(jb + 1) % kRing]);
               sacc[(jb + 1) & 1] = qk_block(kreg[(jb + 1) & 1], mcb[msel(jb + 1)],
                                             pops(std::integral_constant<int, jb + 1>{}));
+            }
           }
           // the K operands of block jb + 2 are read only when it exists
           const bool pre_live = jb + 2 < nblk;
@@ -758,9 +829,11 @@ static hipError_t launch_fwd_t(const FwdArgs& a_in, hipStream_t stream) {
   const int grid = a.B * a.H * a.i_tiles * a.n_groups;
   // the balanced work order: a mask to rank the batch entries by (one wave's
   // lanes cover every entry's blocks), two workgroups per CU in one round (not
-  // the three-wave tiles), and units that split evenly over the XCDs' halves
+  // the three-wave tiles), units that split evenly over the XCDs' halves, and
+  // not a streamed pair bias (which has an order of its own)
   a.balance = 0;
-  if (HM && a.mask != nullptr && !kFwdThreeWaves<D, HP> && a.B >= 2 && a.B <= kBalanceMaxB &&
+  const bool streamed = HP && a.L > KVTile<D>::CH;
+  if (HM && a.mask != nullptr && !kFwdThreeWaves<D, HP> && !streamed && a.B >= 2 && a.B <= kBalanceMaxB &&
       a.B * ((a.L + 31) / 32) <= 64 && a.ncu > 0 && grid == 2 * a.ncu && grid % 8 == 0) {
     const int per = grid / 8, unit = a.H * a.i_tiles;
     if (per % (2 * unit) == 0) a.balance = 1;
