@@ -167,11 +167,16 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
         v[0] = t4[0] | (t4[1] << 16);
         v[1] = t4[2] | (t4[3] << 16);
       }
-      if constexpr (kPairMfma) {
-        v[0] = bf16x2_no_neg_inf(v[0]);
-        v[1] = bf16x2_no_neg_inf(v[1]);
-      }
       pbias[blk] = v;
+    }
+    // after all the loads: a clamp next to its load would wait for each load
+    // in turn
+    if constexpr (kPairMfma) {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        pbias[blk][0] = bf16x2_no_neg_inf(pbias[blk][0]);
+        pbias[blk][1] = bf16x2_no_neg_inf(pbias[blk][1]);
+      }
     }
   }
   // A operands of the bias product: the parts of sqrt(D) on the diagonal,

@@ -277,8 +277,14 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
           }
         __syncthreads();  // the slab area is reused by the K/V tiles
       } else {
+        // all loads first, then the -inf clamp (keys past L: the mask term,
+        // always present when L is not a multiple of 32, makes them -inf)
 #pragma unroll
-        for (int kb = 0; kb < RES; ++kb) load_pair_ops<kPairMfma>(pres[kb], prow, kb * 32, L, half, pvec);
+        for (int kb = 0; kb < RES; ++kb) load_pair_ops<kPairMfma, false>(pres[kb], prow, kb * 32, L, half, pvec);
+        if constexpr (kPairMfma) {
+#pragma unroll
+          for (int kb = 0; kb < RES; ++kb) pair_no_neg_inf(pres[kb]);
+        }
       }
     }
   }
@@ -643,7 +649,9 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
   // before the block that uses it (across tile boundaries: the pair bias
   // does not depend on n).  Against loading a whole tile's bias at the top of
   // the tile, this holds half the registers and takes no load latency at the
-  // start of a tile (measured on MI355X at (1,768,768,4,32): forward -25%).
+  // start of a tile; the loads leave their values as they arrive (no wait at
+  // the load; measured on MI355X at (1,768,768,4,32), with the work order of
+  // a streamed bias: forward 908 -> 757 us).
   constexpr bool kStream = RES == 0 && HAS_PAIR;
   constexpr int kRing = 4;
   short8_t pring[kStream ? kRing : 1][2];
