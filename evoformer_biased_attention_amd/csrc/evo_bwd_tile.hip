@@ -625,6 +625,36 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
       pbias[qb] = __builtin_bit_cast(u32x2, lds_read_tr_b(src, (row * kRows + kcol) * 2));
     }
   };
+  // Rows longer than one query tile (MULTI), L % 8 == 0: the slab is split by
+  // wave, each wave's region holding only its own 16 bias columns (CH rows of
+  // 32 bytes, contiguous), so a wave refills its region as soon as it has
+  // read it, with no workgroup barrier between its reads and the next copy
+  // (and the regions' 32-byte rows keep a transposed read's four rows on
+  // different banks).
+  auto issue_slab_w = [&](int q0) {
+    uint8_t* dst = sslab + wave * (TL::CH * 32);
+#pragma unroll
+    for (int i = 0; i < TL::CH * 2 / 64; ++i) {
+      const int c = 64 * i + lane;  // 16-byte chunk c: row c / 2, keys 8 (c % 2) ..
+      const uint16_t* src =
+          pbase + (size_t)min(q0 + (c >> 1), L - 1) * L + min(kc0k + 16 * wave + 8 * (c & 1), L - 8);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(dst + 64 * 16 * i), 16, 0, 0);
+    }
+  };
+  // the wave's region into pbias (reads the compiler does not track, so it
+  // does not wait for the copies in flight; the wait below completes them)
+  auto read_slab_w = [&]() {
+    const uint8_t* src = sslab + wave * (TL::CH * 32);
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      const int row = 16 * qb + 4 * g + (col >> 2);
+      pbias[qb] = __builtin_bit_cast(u32x2, lds_read_tr_asm(src, (row * 16 + 4 * (col & 3)) * 2));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) asm volatile("" : "+v"(pbias[qb]));
+  };
   auto gather_bias = [&](int q0) {  // L % 8 != 0: column reads straight from memory
     const uint16_t* prow = pbase + jc;
 #pragma unroll
@@ -738,7 +768,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
     load_rows(n_begin, 0);
     issue_qo(0, 0);
     if constexpr (MULTI && HAS_PAIR) {
-      if ((L % 8) == 0) issue_slab(sslab, 0);
+      if ((L % 8) == 0) issue_slab_w(0);
     }
     store_rows(0);
     vm_wait_all();
@@ -762,10 +792,9 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
       dmsum = 0.f;
     }
     if constexpr (MULTI && HAS_PAIR) {
-      // this tile's bias columns; the slab is then free for the next tile's
+      // this tile's bias columns; the wave's region is then free for the next tile's
       if ((L % 8) == 0) {
-        read_slab(sslab);
-        lds_barrier();
+        read_slab_w();
       } else {
         gather_bias(q0);
       }
@@ -774,7 +803,7 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
       const int n1 = n_begin + (u + 1) / qtiles, qt1 = (u + 1) % qtiles;
       issue_qo(u + 1, (u + 1) & 1);
       if constexpr (MULTI && HAS_PAIR) {
-        if ((L % 8) == 0) issue_slab(sslab, qt1 * TL::CH);
+        if ((L % 8) == 0) issue_slab_w(qt1 * TL::CH);
       }
       load_rows(n1, qt1 * TL::CH);
       if (qt1 == 0) load_keys(n1);
