@@ -574,9 +574,8 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   constexpr int KC = TL::KC, VC = TL::VC;
   constexpr int NT = 64 * NW, kRows = 16 * NW;
   constexpr int kSlab = HAS_PAIR ? TL::CH * kRows * 2 : 0;  // pair[CH queries][the workgroup's keys]
-  constexpr int kSmem = (MULTI || 2 * TL::BUF_BYTES > kSlab) ? 2 * TL::BUF_BYTES : kSlab;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
-  __shared__ __attribute__((aligned(16))) uint8_t sslab[(MULTI && HAS_PAIR) ? kSlab : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sslab[HAS_PAIR ? kSlab : 16];
   __shared__ __attribute__((aligned(16))) float slse[2][TL::CH];  // -lse log2e; -inf past L / no finite score
   __shared__ __attribute__((aligned(16))) float sndel[2][TL::CH]; // -delta
 
@@ -603,34 +602,15 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   const uint16_t* pbase = HAS_PAIR ? a.pair + ((size_t)b * H + h) * L * L : nullptr;
   const int kc0k = jt * kRows;  // the workgroup's first key
 
-  // pair[q0 + 0..CH)[the workgroup's keys] row-major (2 kRows-byte rows) into
-  // an LDS slab by 16-byte copies (L % 8 == 0)
-  auto issue_slab = [&](uint8_t* dst, int q0) {
-    constexpr int RC = kRows / 8;  // 16-byte chunks per slab row
-    for (int base = wave * 64; base < TL::CH * RC; base += NT) {
-      const int q = base + lane;
-      const int r = q / RC, c = q % RC;
-      const uint16_t* src = pbase + (size_t)min(q0 + r, L - 1) * L + min(kc0k + 8 * c, L - 8);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(dst + base * 16), 16, 0, 0);
-    }
-  };
   // bias block qb of a query tile: lane gets pair[q0 + 16 qb + 4 g + r][j], r = 0..3
   u32x2 pbias[HAS_PAIR ? NB : 1];
-  auto read_slab = [&](const uint8_t* src) {
-#pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
-      const int row = 16 * qb + 4 * g + (col >> 2);
-      const int kcol = wave * 16 + 4 * (col & 3);
-      pbias[qb] = __builtin_bit_cast(u32x2, lds_read_tr_b(src, (row * kRows + kcol) * 2));
-    }
-  };
-  // Rows longer than one query tile (MULTI), L % 8 == 0: the slab is split by
-  // wave, each wave's region holding only its own 16 bias columns (CH rows of
-  // 32 bytes, contiguous), so a wave refills its region as soon as it has
-  // read it, with no workgroup barrier between its reads and the next copy
-  // (and the regions' 32-byte rows keep a transposed read's four rows on
-  // different banks).
+  // The bias columns of a query tile (L % 8 == 0) come through an LDS slab
+  // split by wave, each wave's region holding only its own 16 columns (CH rows
+  // of 32 bytes, contiguous), so a wave reads its region as soon as its own
+  // copies are done, and (rows longer than one query tile) refills it as soon
+  // as it has read it, with no workgroup barrier; the regions' 32-byte rows
+  // keep a transposed read's four rows on different banks.  The slab has LDS
+  // of its own, so its first copy goes out with the first Q and dO tile.
   auto issue_slab_w = [&](int q0) {
     uint8_t* dst = sslab + wave * (TL::CH * 32);
 #pragma unroll
@@ -667,17 +647,10 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
     }
   };
 
-  // ---- resident pair bias (one query tile)
+  // ---- resident pair bias (one query tile), rows of odd length (the slab's
+  // are read after the prologue's copies)
   if constexpr (HAS_PAIR && !MULTI) {
-    if ((L % 8) == 0) {
-      issue_slab(smem, 0);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      read_slab(smem);
-      __syncthreads();
-    } else {
-      gather_bias(0);
-    }
+    if ((L % 8) != 0) gather_bias(0);
   }
 
   // ones in row 0 of the column-sum operand
@@ -767,12 +740,15 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
     load_keys(n_begin);
     load_rows(n_begin, 0);
     issue_qo(0, 0);
-    if constexpr (MULTI && HAS_PAIR) {
+    if constexpr (HAS_PAIR) {
       if ((L % 8) == 0) issue_slab_w(0);
     }
     store_rows(0);
     vm_wait_all();
     take_keys();
+    if constexpr (HAS_PAIR && !MULTI) {
+      if ((L % 8) == 0) read_slab_w();  // its own copies are done
+    }
   }
   // The next step's copies and loads are completed, and its rows and keys
   // taken, before this step's dK, dV stores are issued: no wait (a barrier's
