@@ -169,15 +169,6 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
       }
       pbias[blk] = v;
     }
-    // after all the loads: a clamp next to its load would wait for each load
-    // in turn
-    if constexpr (kPairMfma) {
-#pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        pbias[blk][0] = bf16x2_no_neg_inf(pbias[blk][0]);
-        pbias[blk][1] = bf16x2_no_neg_inf(pbias[blk][1]);
-      }
-    }
   }
   // A operands of the bias product: the parts of sqrt(D) on the diagonal,
   // lane (key row col, group g) holding A[col][4 g + e]
@@ -310,6 +301,17 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     store_mask(0, lk);
     vm_wait_all();
     take_rows(n_begin);
+  }
+  // the bias loads' -inf clamp once they and the first tile's copies are in
+  // (a clamp next to its load would wait for each load in turn, and one
+  // before the copies would hold the copies back; measured within the noise
+  // at (1,512,256,8,8) and (1,768,768,4,32) against the clamps before them)
+  if constexpr (kPairMfma) {
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      pbias[blk][0] = bf16x2_no_neg_inf(pbias[blk][0]);
+      pbias[blk][1] = bf16x2_no_neg_inf(pbias[blk][1]);
+    }
   }
   // The next slice's copies and row loads are completed before this slice's
   // dQ stores are issued.  With SPLIT (one key tile of a longer row per
