@@ -135,6 +135,10 @@ PAIR_INF = [
     I.custom("pinf_l96_d64_bf16", 1, 2, 96, 2, 64, "bf16", None, 1.0, 74),
     I.custom("pinf_l40_d8_bf16", 1, 3, 40, 2, 8, "bf16", 0.1, 1.0, 75),
     I.custom("pinf_l100_d32_fp16", 1, 3, 100, 2, 32, "fp16", 0.05, 1.0, 76),
+    # rows longer than one key tile with vector bias loads: the forward's bias
+    # ring and bwd_kv3's per-wave bias regions (bf16 and fp16)
+    I.custom("pinf_l320_d32_bf16_streamed_vec", 1, 2, 320, 2, 32, "bf16", 0.05, 1.0, 77),
+    I.custom("pinf_l264_d32_fp16_streamed", 1, 2, 264, 2, 32, "fp16", 0.05, 1.0, 78),
 ]
 
 
