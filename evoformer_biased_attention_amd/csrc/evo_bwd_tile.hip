@@ -324,6 +324,29 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
   // slice unless KLOOP); dQ accumulates over a slice's key tiles.
   const int nsteps = ntiles * kjt;
   floatx4 dq[MB];
+  // dQ = scale * dQ^T of slice n (after its last key tile): lane holds
+  // d = 16 mb + 4 g + 0..3 of query i
+  auto store_dq = [&](int n) {
+    if (!i_valid) return;
+    // dense row index of the fp32 partials (slices of the chunk)
+    const size_t row = (((size_t)b * a.q_nc + (n - a.q_n0)) * L + i) * H + h;
+    const int64_t qoff = b * a.sB + n * a.sN + i * a.sL + h * D;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int d = 16 * mb + 4 * g;
+      if (d < D) {
+        if constexpr (SPLIT) {
+          float* dst = a.dq_part + ((size_t)jt * a.B * a.q_nc * L * H + row) * D + d;
+          *reinterpret_cast<floatx4*>(dst) = dq[mb] * scale;
+        } else {
+          u32x2 w;
+          w[0] = T::pack2(dq[mb][0] * scale, dq[mb][1] * scale);
+          w[1] = T::pack2(dq[mb][2] * scale, dq[mb][3] * scale);
+          *reinterpret_cast<u32x2*>(a.dq + qoff + d) = w;
+        }
+      }
+    }
+  };
   for (int t = 0; t < nsteps; ++t) {
     const int n = n_begin + t / kjt;
     const int jts = t % kjt;  // the step's key tile (0 unless KLOOP)
@@ -335,7 +358,10 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
     } else {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (t > 0 && jts == 0) take_rows(n);
+      if (t > 0 && jts == 0) {
+        store_dq(n - 1);  // the previous slice's (its dq registers are cleared below)
+        take_rows(n);
+      }
     }
     if (t1 < nsteps) {
       if constexpr (KLOOP) {
@@ -517,27 +543,15 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
       store_mask(t1 & 1, lk - jt1 * TL::CH);  // its buffer was last read during step t-1
       if constexpr (SPLIT) take_rows(n + 1);
     }
-    // ---- dQ = scale * dQ^T (after a slice's last key tile): lane holds d = 16 mb + 4 g + 0..3 of query i
-    if (i_valid && jts == kjt - 1) {
-      // dense row index of the fp32 partials (slices of the chunk)
-      const size_t row = (((size_t)b * a.q_nc + (n - a.q_n0)) * L + i) * H + h;
-      const int64_t qoff = b * a.sB + n * a.sN + i * a.sL + h * D;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int d = 16 * mb + 4 * g;
-        if (d < D) {
-          if constexpr (SPLIT) {
-            float* dst = a.dq_part + ((size_t)jt * a.B * a.q_nc * L * H + row) * D + d;
-            *reinterpret_cast<floatx4*>(dst) = dq[mb] * scale;
-          } else {
-            u32x2 w;
-            w[0] = T::pack2(dq[mb][0] * scale, dq[mb][1] * scale);
-            w[1] = T::pack2(dq[mb][2] * scale, dq[mb][3] * scale);
-            *reinterpret_cast<u32x2*>(a.dq + qoff + d) = w;
-          }
-        }
-      }
+    // SPLIT: the slice's dQ partial now (the next step's barrier waits for
+    // LDS only); otherwise after the next step's barrier, which waits for
+    // all memory operations and would otherwise wait for these stores
+    if constexpr (SPLIT) {
+      if (jts == kjt - 1) store_dq(n);
     }
+  }
+  if constexpr (!SPLIT) {
+    if (nsteps > 0) store_dq(n_begin + (nsteps - 1) / kjt);  // the last slice's
   }
 
   if constexpr (WANT_DPAIR && !SPLIT) {
