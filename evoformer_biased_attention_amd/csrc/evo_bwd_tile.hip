@@ -21,7 +21,8 @@
 //   - the mask enters the score MFMA as its accumulator input (sqrt(D) * mask,
 //     -inf for keys past L), so it costs neither a VALU op nor an MFMA;
 //   - -delta enters the dP MFMA the same way, so dS = P * acc is one multiply;
-//   - the n-sum of dpair is an MFMA against an identity operand;
+//   - the n-sum of dpair is an MFMA against an identity operand (fp16; bf16
+//     adds the fp32 dS in place);
 //   - LDS operand reads use the instruction's immediate offset field;
 //   - keys masked with -inf have P = dS = 0: bwd_q3 stops a slice's steps at
 //     the tile's last key that is not -inf (the padding at the end of a row
@@ -574,12 +575,14 @@ __global__ __launch_bounds__(64 * NW) void evo_bwd_q3_kernel(BwdArgs a) {
 //   P = exp2(...),  dS = P dP
 //   dV^T += dO^T P,  dK^T += Q^T dS      (dO^T, Q^T by transposed LDS reads)
 //   dmask partial += column sums of dS   (MFMA against a row of ones)
-// Rows that fit one query tile: the pair-bias columns of the workgroup's keys
-// are read once per workgroup (through LDS, transposed) and stay in registers
-// for the whole n-group.  Longer rows (MULTI): per n the queries come in
-// tiles of CH; dK, dV and dmask accumulate over the tiles, and the bias
-// columns of each (n, tile) are staged through a slab of their own while the
-// previous tile is computed.
+// The pair-bias columns of the workgroup's keys come through an LDS slab of
+// their own, split by wave (each wave's 16 columns), read with transposed
+// reads.  Rows that fit one query tile: read once per workgroup, their copy
+// beside the first Q and dO tile, and kept in registers for the whole n-group.
+// Longer rows (MULTI): per n the queries come in tiles of CH; dK, dV and dmask
+// accumulate over the tiles, and each (n, tile)'s columns are copied while the
+// previous tile is computed, each wave refilling its region as soon as it has
+// read it.
 template <class T, int D, bool HAS_PAIR, bool WANT_DMASK, bool MULTI, int NW>
 __global__ __launch_bounds__(64 * NW) void evo_bwd_kv3_kernel(BwdArgs a) {
   using TL = KVTile<D>;

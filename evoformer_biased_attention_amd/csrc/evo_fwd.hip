@@ -17,7 +17,8 @@
 //     fetched from LDS by transposed reads.
 //   The pair bias does not depend on n.  When a row of it fits in registers
 //   (L <= 256) each wave loads its 32 rows once and reuses them for all G
-//   slices; otherwise it is re-read from L2 for every block.
+//   slices; otherwise each block's values are loaded from L2 three blocks
+//   ahead into a ring of four blocks' registers.
 //   The mask bias is the QK^T product's accumulator input: per tile an fp32
 //   row of sqrt(D)*mask[j] (-inf for keys past L) sits in LDS, and each block
 //   starts its S^T accumulator from it, so the scale turns it back into
