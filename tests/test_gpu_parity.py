@@ -38,6 +38,10 @@ SMALL = [
     I.custom("l384_mask_only_bf16", 1, 3, 384, 2, 16, "bf16", 0.1, None, 25),
     I.custom("l260_d64_gathered_bias", 1, 2, 260, 2, 64, "fp16", 0.1, 1.0, 26),
     I.custom("l513_d8_bf16", 1, 2, 513, 1, 8, "bf16", 0.05, 1.0, 27),
+    # bf16 pair bias on rows longer than one key tile, L % 8 == 0 (vector bias
+    # loads: the forward's bias ring, the key side's bias regions) at D = 8, 16
+    I.custom("l320_d8_bf16_pair", 1, 2, 320, 2, 8, "bf16", 0.05, 1.0, 28),
+    I.custom("l264_d16_bf16_pair", 1, 3, 264, 1, 16, "bf16", 0.05, 1.0, 29),
 ]
 
 
