@@ -17,8 +17,8 @@
 //     fetched from LDS by transposed reads.
 //   The pair bias does not depend on n.  When a row of it fits in registers
 //   (L <= 256) each wave loads its 32 rows once and reuses them for all G
-//   slices; otherwise each block's values are loaded from L2 three blocks
-//   ahead into a ring of four blocks' registers.
+//   slices; otherwise each block's values are loaded from L2 seven blocks
+//   ahead (three at D = 64) into a ring of registers.
 //   The mask bias is the QK^T product's accumulator input: per tile an fp32
 //   row of sqrt(D)*mask[j] (-inf for keys past L) sits in LDS, and each block
 //   starts its S^T accumulator from it, so the scale turns it back into
@@ -648,13 +648,13 @@ __global__ __launch_bounds__(256, (kFwdThreeWaves<D, HAS_PAIR> ? 3 : 2)) void ev
   // Streamed pair bias (rows longer than one key tile): a ring of kRing
   // blocks' values, block j in slot j % kRing, each loaded kRing - 1 blocks
   // before the block that uses it (across tile boundaries: the pair bias
-  // does not depend on n).  Against loading a whole tile's bias at the top of
-  // the tile, this holds half the registers and takes no load latency at the
-  // start of a tile; the loads leave their values as they arrive (no wait at
-  // the load; measured on MI355X at (1,768,768,4,32), with the work order of
-  // a streamed bias: forward 908 -> 757 us).
+  // does not depend on n), so no load latency falls at the start of a tile;
+  // the loads leave their values as they arrive (no wait at the load).
+  // Measured on MI355X at (1,768,768,4,32), with the work order of a streamed
+  // bias: forward 908 us loading each tile's bias at its top, 757 us with a
+  // ring of 4, 728 us with 8 (803 with 2).
   constexpr bool kStream = RES == 0 && HAS_PAIR;
-  constexpr int kRing = 4;
+  constexpr int kRing = TL::CH / 32 >= 8 ? 8 : 4;  // a tile's blocks (it must divide them)
   short8_t pring[kStream ? kRing : 1][2];
   // the next tile's copies go out in the middle of a streamed tile, after the
   // bias loads of the blocks before it: waiting for those never waits for
